@@ -1,0 +1,172 @@
+"""Fine-grained FP8 quantization and block-scaled GEMMs for MI355X (gfx950).
+
+Thin ctypes binding over libfp8fg.so (HIP kernels + C ABI, declared in include/fp8fg.h). The Python
+functions carry the C names and only marshal arguments: torch tensors provide device memory and the
+current HIP stream; every step of the computation runs in the library's kernels. There is no CPU
+fallback: if the library is missing or the tensors are not on a GPU, the calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8fg.so")
+
+FG_SCALE_FP32, FG_SCALE_POW2 = 0, 1
+FG_OUT_F32, FG_OUT_BF16 = 0, 1
+FG_ALONG_COLS, FG_ALONG_ROWS = 0, 1
+
+_lib = None
+
+
+class Fp8fgError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libfp8fg.so (built in-tree by fp8_fine_grained_amax_amd/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Fp8fgError(f"{LIB_PATH} is not built; run fp8_fine_grained_amax_amd/build.py (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int32
+        L.fg_quantize_act_1x128.argtypes = [P, I64, I64, I64, I, I, P, P, P]
+        L.fg_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P, P]
+        L.fg_fp8_gemm_fprop.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+        L.fg_fp8_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+        L.fg_fp8_gemm_wgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+        L.fg_fp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, P]
+        for f in ("fg_quantize_act_1x128", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop", "fg_fp8_gemm_dgrad",
+                  "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm"):
+            getattr(L, f).restype = I
+        L.fg_status_string.argtypes = [I]
+        L.fg_status_string.restype = ctypes.c_char_p
+        L.fg_last_hip_error.argtypes = []
+        L.fg_last_hip_error.restype = I
+        _lib = L
+    return _lib
+
+
+def fg_status_string(status: int) -> str:
+    return lib().fg_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        extra = f" (hipError {lib().fg_last_hip_error()})" if status == 4 else ""
+        raise Fp8fgError(f"{what}: {fg_status_string(status)}{extra}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise Fp8fgError("fp8fg operates on GPU tensors only")
+
+
+def _out_code(dtype):
+    if dtype == torch.float32:
+        return FG_OUT_F32
+    if dtype == torch.bfloat16:
+        return FG_OUT_BF16
+    raise Fp8fgError(f"output dtype must be float32 or bfloat16, got {dtype}")
+
+
+def fg_quantize_act_1x128(x, axis: int = FG_ALONG_COLS, pow2: bool = False, q=None, scales=None):
+    """1x128 E4M3 quantization of a bf16 matrix x [rows, cols] (row stride may exceed cols).
+
+    axis FG_ALONG_COLS: returns q uint8 [rows, cols], scales f32 [cols/128, rows].
+    axis FG_ALONG_ROWS (token dim): returns q uint8 [cols, rows] (transposed), scales f32 [rows/128, cols].
+    """
+    _gpu(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise Fp8fgError("x must be a 2-D bf16 tensor with unit column stride")
+    rows, cols = x.shape
+    if axis == FG_ALONG_COLS:
+        qshape, sshape = (rows, cols), ((cols + 127) // 128, rows)
+    else:
+        qshape, sshape = (cols, rows), ((rows + 127) // 128, cols)
+    if q is None:
+        q = torch.empty(qshape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    _check(lib().fg_quantize_act_1x128(_ptr(x), rows, cols, x.stride(0), int(axis),
+                                       FG_SCALE_POW2 if pow2 else FG_SCALE_FP32, _ptr(q), _ptr(scales),
+                                       _stream(x.device)), "fg_quantize_act_1x128")
+    return q, scales
+
+
+def fg_quantize_w_128x128(w, pow2: bool = False, q=None, scales=None):
+    """128x128-block E4M3 quantization of a bf16 weight w [n, k]: q uint8 [n, k], scales f32 [ceil(n/128), k/128]."""
+    _gpu(w)
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or w.stride(1) != 1:
+        raise Fp8fgError("w must be a 2-D bf16 tensor with unit column stride")
+    n, k = w.shape
+    if q is None:
+        q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(((n + 127) // 128, (k + 127) // 128), dtype=torch.float32, device=w.device)
+    _check(lib().fg_quantize_w_128x128(_ptr(w), n, k, w.stride(0), FG_SCALE_POW2 if pow2 else FG_SCALE_FP32,
+                                       _ptr(q), _ptr(scales), _stream(w.device)), "fg_quantize_w_128x128")
+    return q, scales
+
+
+def fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None):
+    """Y [M, N] = X [M, K] . W [N, K]^T from E4M3 codes and their scales."""
+    _gpu(xq, sx, wq, sw, y)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _check(lib().fg_fp8_gemm_fprop(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _out_code(y.dtype),
+                                   _stream(xq.device)), "fg_fp8_gemm_fprop")
+    return y
+
+
+def fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.float32, dx=None):
+    """dX [M, K] = dY [M, N] . W [N, K], contracting over N, with W's codes and 128x128 block scales."""
+    _gpu(dyq, sdy, wq, sw, dx)
+    M, N = dyq.shape
+    K = wq.shape[1]
+    if dx is None:
+        dx = torch.empty((M, K), dtype=out_dtype, device=dyq.device)
+    _check(lib().fg_fp8_gemm_dgrad(_ptr(dyq), _ptr(sdy), _ptr(wq), _ptr(sw), M, N, K, _ptr(dx), _out_code(dx.dtype),
+                                   _stream(dyq.device)), "fg_fp8_gemm_dgrad")
+    return dx
+
+
+def fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False):
+    """dW [N, K] (+)= dY^T . X from token-dim quantized dYt [N, M] and Xt [K, M]; fp32 output."""
+    _gpu(dytq, sdyt, xtq, sxt, dw)
+    N, M = dytq.shape
+    K = xtq.shape[0]
+    if dw is None:
+        if accumulate:
+            raise Fp8fgError("accumulate needs an existing dw")
+        dw = torch.empty((N, K), dtype=torch.float32, device=dytq.device)
+    _check(lib().fg_fp8_gemm_wgrad(_ptr(dytq), _ptr(sdyt), _ptr(xtq), _ptr(sxt), M, N, K, _ptr(dw), int(bool(accumulate)),
+                                   _stream(dytq.device)), "fg_fp8_gemm_wgrad")
+    return dw
+
+
+def fg_fp8_grouped_gemm(xq, sx, wq, sw, offsets, out_dtype=torch.bfloat16, y=None):
+    """Per group g: Y[off[g]:off[g+1]] = X[off[g]:off[g+1]] . W[g]^T. offsets: device int32 [G+1]."""
+    _gpu(xq, sx, wq, sw, offsets, y)
+    if offsets.dtype != torch.int32:
+        raise Fp8fgError("offsets must be int32")
+    T, K = xq.shape
+    G, N, _ = wq.shape
+    if y is None:
+        y = torch.empty((T, N), dtype=out_dtype, device=xq.device)
+    _check(lib().fg_fp8_grouped_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(offsets), G, T, N, K, _ptr(y),
+                                     _out_code(y.dtype), _stream(xq.device)), "fg_fp8_grouped_gemm")
+    return y

@@ -1,0 +1,140 @@
+// C-ABI entry points of libfp8fg: host-side argument checks, then one kernel launch on the caller's
+// stream. Declarations, layouts and error behaviour: include/fp8fg.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8fg.h"
+
+hipError_t fg_launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
+                                    uint8_t* q, float* scales, hipStream_t stream);
+hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
+                                    uint8_t* q, float* scales, hipStream_t stream);
+hipError_t fg_launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ld, int pow2, uint8_t* q,
+                             float* scales, hipStream_t stream);
+hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                                int64_t N, int64_t K, void* y, int out_bf16, hipStream_t stream);
+hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
+                                int64_t N, int64_t K, void* dx, int out_bf16, hipStream_t stream);
+hipError_t fg_launch_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
+                                int64_t M, int64_t N, int64_t K, float* dw, int accumulate, hipStream_t stream);
+hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                  const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, void* y,
+                                  int out_bf16, hipStream_t stream);
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Grid limits of the launchers: 2^31-1 workgroups in x, 65535 in y.
+constexpr int64_t kMaxGridX = 2147483647LL;
+constexpr int64_t kMaxGridY = 65535LL;
+constexpr int64_t kMaxGemmTiles = 2147483647LL;
+constexpr int32_t kMaxGroups = 65536;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+fg_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return FG_OK;
+    g_last_hip_error = (int)e;
+    return FG_ERR_HIP;
+}
+
+bool valid_mode(int m) { return m == FG_SCALE_FP32 || m == FG_SCALE_POW2; }
+bool valid_out(int o) { return o == FG_OUT_F32 || o == FG_OUT_BF16; }
+
+int64_t tiles(int64_t a, int64_t b) { return ((a + 255) / 256) * ((b + 255) / 256); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fg_status_string(fg_status s) {
+    switch (s) {
+        case FG_OK: return "ok";
+        case FG_ERR_INVALID_ARG: return "invalid argument";
+        case FG_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case FG_ERR_MISALIGNED: return "misaligned pointer or leading dimension";
+        case FG_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int fg_last_hip_error(void) { return g_last_hip_error; }
+
+fg_status fg_quantize_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ld_x, fg_tile_axis axis,
+                                fg_scale_mode mode, uint8_t* q, float* scales, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || !valid_mode(mode) || (axis != FG_ALONG_COLS && axis != FG_ALONG_ROWS))
+        return FG_ERR_INVALID_ARG;
+    if (ld_x < cols) return FG_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return FG_OK;
+    if (!x || !q || !scales) return FG_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(scales) || (ld_x % 8) != 0) return FG_ERR_MISALIGNED;
+    const int pow2 = mode == FG_SCALE_POW2;
+    if (axis == FG_ALONG_COLS) {
+        if (cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+        if (cols / 128 > kMaxGridY || (rows + 63) / 64 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+        return from_hip(fg_launch_quant_act_cols((const uint16_t*)x, rows, cols, ld_x, pow2, q, scales, stream));
+    }
+    if (rows % 128 != 0 || cols % 8 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (rows / 128 > kMaxGridY || (cols + 63) / 64 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    return from_hip(fg_launch_quant_act_rows((const uint16_t*)x, rows, cols, ld_x, pow2, q, scales, stream));
+}
+
+fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_w, fg_scale_mode mode, uint8_t* q,
+                                float* scales, hipStream_t stream) {
+    if (n < 0 || k < 0 || !valid_mode(mode) || ld_w < k) return FG_ERR_INVALID_ARG;
+    if (n == 0 || k == 0) return FG_OK;
+    if (!w || !q || !scales) return FG_ERR_INVALID_ARG;
+    if (k % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(w) || !aligned16(q) || !aligned4(scales) || (ld_w % 8) != 0) return FG_ERR_MISALIGNED;
+    if ((n + 127) / 128 > kMaxGridY || k / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    return from_hip(fg_launch_quant_w((const uint16_t*)w, n, k, ld_w, mode == FG_SCALE_POW2, q, scales, stream));
+}
+
+fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                            int64_t N, int64_t K, void* y, fg_out_dtype out, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || !valid_out(out)) return FG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return FG_OK;
+    if (!y || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
+    if (K % 128 != 0 || tiles(M, N) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw)) return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_gemm_fprop(xq, sx, wq, sw, M, N, K, y, out == FG_OUT_BF16, stream));
+}
+
+fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
+                            int64_t N, int64_t K, void* dx, fg_out_dtype out, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || !valid_out(out)) return FG_ERR_INVALID_ARG;
+    if (M == 0 || K == 0) return FG_OK;
+    if (!dx || (N > 0 && (!dyq || !sdy || !wq || !sw))) return FG_ERR_INVALID_ARG;
+    if (N % 128 != 0 || K % 128 != 0 || tiles(M, K) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(dyq) || !aligned16(wq) || !aligned16(dx) || !aligned4(sdy) || !aligned4(sw)) return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_gemm_dgrad(dyq, sdy, wq, sw, M, N, K, dx, out == FG_OUT_BF16, stream));
+}
+
+fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt, int64_t M,
+                            int64_t N, int64_t K, float* dw, int accumulate, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0) return FG_ERR_INVALID_ARG;
+    if (N == 0 || K == 0) return FG_OK;
+    if (!dw || (M > 0 && (!dytq || !sdyt || !xtq || !sxt))) return FG_ERR_INVALID_ARG;
+    if (M % 128 != 0 || K % 4 != 0 || tiles(N, K) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(dytq) || !aligned16(xtq) || !aligned16(dw) || !aligned16(sxt) || !aligned4(sdyt))
+        return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_gemm_wgrad(dytq, sdyt, xtq, sxt, M, N, K, dw, accumulate != 0, stream));
+}
+
+fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                              const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K, void* y,
+                              fg_out_dtype out, hipStream_t stream) {
+    if (G < 1 || G > kMaxGroups || total_rows < 0 || N < 0 || K < 0 || !valid_out(out)) return FG_ERR_INVALID_ARG;
+    if (total_rows == 0 || N == 0) return FG_OK;
+    if (!y || !d_offsets || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
+    if (K % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (((total_rows + 255) / 256 + G) * ((N + 255) / 256) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw) || !aligned4(d_offsets))
+        return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_gemm_grouped(xq, sx, wq, sw, d_offsets, G, total_rows, N, K, y, out == FG_OUT_BF16,
+                                           stream));
+}
+
+}  // extern "C"

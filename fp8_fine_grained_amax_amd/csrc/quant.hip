@@ -1,0 +1,234 @@
+// Online E4M3 quantization kernels for gfx950: 1x128 activation tiles (along columns, or along the token
+// dimension with a transposed write) and 128x128 weight blocks.
+//
+// Each kernel reads the bf16 input from HBM exactly once, finds the group's max-abs on chip, derives the
+// fp32 scale and writes E4M3 codes plus the scale. The operation is HBM-bound (2 B read + 1 B written
+// per element, + 4 B per group), so the kernels are built around wide coalesced accesses, several
+// 16-byte loads in flight per lane, and reductions that stay in registers (DPP) or a tiny LDS array.
+//
+// Sources: the fine-grained scaling (1x128 tiles for activations, 128x128 blocks for weights) is Figure 7
+// (a) as quoted on the pages "Three Fast Methods To Study Deepseek" and the untitled cameseeing.com and
+// why-be.why-be.co.kr pages; the online max-abs per tile/block and the online quantization are from the
+// cameseeing.com page's passage next to that figure; the alignment of the max-abs to the largest FP8
+// value from "5 Ways You can get More Deepseek While Spending Less" (paragraph on per-group scaling);
+// power-of-2 scales from the opening paragraph of that page.
+#include "common.h"
+
+// ------------------------------------------------------------------------------------------------
+// 1x128 tiles along columns.
+// One 1x128 bf16 tile is 256 B = 16 lanes x 16 B, i.e. exactly one DPP row, so the tile max-abs is four
+// DPP steps with no LDS. A 256-thread workgroup covers 16 rows of one 128-column group per unrolled
+// slot; blockIdx.y is the column group, so the 16 scales of a slot are one contiguous 64 B write in the
+// MN-major scale layout [cols/128][rows].
+// ------------------------------------------------------------------------------------------------
+template <int UNROLL>
+__global__ __launch_bounds__(256) void fg_quant_act_cols_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t ld, int pow2, uint8_t* __restrict__ q,
+                                                                int64_t ldq, float* __restrict__ scales) {
+    const int lane16 = threadIdx.x & 15;
+    const int slot = threadIdx.x >> 4;
+    const int64_t g = blockIdx.y;
+    const int64_t r_base = (int64_t)blockIdx.x * (16 * UNROLL) + slot;
+
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; u++) {
+        int64_t r = r_base + 16 * u;
+        if (r < rows)
+            v[u] = *reinterpret_cast<const uint4*>(x + r * ld + g * FG_GROUP + lane16 * 8);
+        else
+            v[u] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; u++) {
+        int64_t r = r_base + 16 * u;
+        uint32_t m = fg_pk_max_u16(fg_pk_max_u16(v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu),
+                                   fg_pk_max_u16(v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu));
+        m = fg_max_halves(fg_row16_max_pk(m));
+        float s = fg_scale_from_amax_bits(m, pow2);
+        fg_divisor d = fg_make_divisor(s);
+        uint32_t lo = fg_cvt2<false>(fg_div(fg_bf16_lo(v[u].x), d), fg_div(fg_bf16_hi(v[u].x), d), 0);
+        lo = fg_cvt2<true>(fg_div(fg_bf16_lo(v[u].y), d), fg_div(fg_bf16_hi(v[u].y), d), lo);
+        uint32_t hi = fg_cvt2<false>(fg_div(fg_bf16_lo(v[u].z), d), fg_div(fg_bf16_hi(v[u].z), d), 0);
+        hi = fg_cvt2<true>(fg_div(fg_bf16_lo(v[u].w), d), fg_div(fg_bf16_hi(v[u].w), d), hi);
+        if (r < rows) {
+            *reinterpret_cast<uint2*>(q + r * ldq + g * FG_GROUP + lane16 * 8) = make_uint2(lo, hi);
+            if (lane16 == 0) scales[g * rows + r] = s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// 1x128 tiles along rows (token dimension), codes written transposed.
+// A 256-thread workgroup owns 128 rows x 64 columns. Thread t reads rows 4*(t/8)+i (i = 0..3) of the
+// 8-column chunk t%8 (16 B per row, coalesced 128 B per row across 8 lanes). Column max-abs: 4 rows in
+// registers, then across the 8 lanes sharing a chunk with lane shuffles, then across the 4 waves in LDS.
+// Codes of one column and 4 consecutive rows pack into one dword (two cvt_pk per dword), go to an LDS
+// transpose buffer [64 cols][128 rows], and leave as 16 B stores: 128 contiguous bytes per column.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fg_quant_act_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t ld, int pow2,
+                                                                uint8_t* __restrict__ q, float* __restrict__ scales) {
+    __shared__ uint32_t colmax[4][32];          // [wave][column pair], packed u16 max-abs
+    __shared__ uint4 codes_t[64 * 8];           // [column][16 B piece], pieces swizzled per column
+
+    const int t = threadIdx.x;
+    const int chunk = t & 7;                    // 8-column chunk within the 64-column tile
+    const int rgrp = t >> 3;                    // rows 4*rgrp .. 4*rgrp+3 within the 128-row tile
+    const int64_t r0 = (int64_t)blockIdx.y * FG_GROUP;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int64_t col = c0 + chunk * 8;
+    const bool col_ok = col < cols;
+
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (col_ok)
+            v[i] = *reinterpret_cast<const uint4*>(x + (r0 + 4 * rgrp + i) * ld + col);
+        else
+            v[i] = make_uint4(0, 0, 0, 0);
+    }
+    // packed max-abs per column pair over this thread's 4 rows
+    uint32_t m[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        uint32_t a = (&v[0].x)[p] & 0x7FFF7FFFu, b = (&v[1].x)[p] & 0x7FFF7FFFu;
+        uint32_t c = (&v[2].x)[p] & 0x7FFF7FFFu, d = (&v[3].x)[p] & 0x7FFF7FFFu;
+        m[p] = fg_pk_max_u16(fg_pk_max_u16(a, b), fg_pk_max_u16(c, d));
+    }
+    // across the 8 lanes of a wave that share this chunk (lane bits 3..5)
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        m[p] = fg_pk_max_u16(m[p], (uint32_t)__shfl_xor((int)m[p], 8));
+        m[p] = fg_pk_max_u16(m[p], (uint32_t)__shfl_xor((int)m[p], 16));
+        m[p] = fg_pk_max_u16(m[p], (uint32_t)__shfl_xor((int)m[p], 32));
+    }
+    const int wave = t >> 6;
+    if ((t & 63) < 8) {
+#pragma unroll
+        for (int p = 0; p < 4; p++) colmax[wave][chunk * 4 + p] = m[p];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        m[p] = fg_pk_max_u16(fg_pk_max_u16(colmax[0][chunk * 4 + p], colmax[1][chunk * 4 + p]),
+                             fg_pk_max_u16(colmax[2][chunk * 4 + p], colmax[3][chunk * 4 + p]));
+    }
+    float s[8];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        s[2 * p] = fg_scale_from_amax_bits(m[p] & 0xFFFFu, pow2);
+        s[2 * p + 1] = fg_scale_from_amax_bits(m[p] >> 16, pow2);
+    }
+    if (rgrp == 0 && col_ok) {
+        float* sp = scales + blockIdx.y * cols + col;
+#pragma unroll
+        for (int j = 0; j < 8; j++) sp[j] = s[j];
+    }
+    // codes: dword j holds column chunk*8+j, rows 4*rgrp .. 4*rgrp+3 (byte i = row i)
+    uint32_t* ct = reinterpret_cast<uint32_t*>(codes_t);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        fg_divisor d = fg_make_divisor(s[j]);
+        float f[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t w = (&v[i].x)[j >> 1];
+            f[i] = fg_div((j & 1) ? fg_bf16_hi(w) : fg_bf16_lo(w), d);
+        }
+        uint32_t dw = fg_cvt2<false>(f[0], f[1], 0);
+        dw = fg_cvt2<true>(f[2], f[3], dw);
+        const int c = chunk * 8 + j;
+        // dword rgrp of column c; the 16 B piece index (rgrp >> 2) is XOR-swizzled by (c >> 3) & 3
+        const int piece = (rgrp >> 2) ^ ((c >> 3) & 3) * 2;
+        ct[c * 32 + piece * 4 + (rgrp & 3)] = dw;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int id = t + 256 * h;             // 512 pieces: column id/8, logical piece id%8
+        const int c = id >> 3, p = id & 7;
+        const int64_t gc = c0 + c;
+        if (gc < cols) {
+            uint4 val = codes_t[c * 8 + (p ^ (((c >> 3) & 3) * 2))];
+            *reinterpret_cast<uint4*>(q + gc * rows + r0 + 16 * p) = val;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// 128x128 weight blocks. One 256-thread workgroup per block: thread t holds rows t/16 + 16 i (i = 0..7)
+// of the 16 B chunk t%16, so each 16-lane group reads one full 256 B block row. The block max-abs is a
+// register max, a DPP row max, two lane shuffles and a 4-entry LDS exchange; the block is read once.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restrict__ w, int64_t n, int64_t ld,
+                                                         int64_t kblocks, int pow2, uint8_t* __restrict__ q,
+                                                         int64_t ldq, float* __restrict__ scales) {
+    __shared__ uint32_t wmax[4];
+    const int t = threadIdx.x;
+    const int chunk = t & 15;
+    const int rsub = t >> 4;
+    const int64_t r0 = (int64_t)blockIdx.y * FG_GROUP;
+    const int64_t c0 = (int64_t)blockIdx.x * FG_GROUP + chunk * 8;
+
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int64_t r = r0 + rsub + 16 * i;
+        if (r < n)
+            v[i] = *reinterpret_cast<const uint4*>(w + r * ld + c0);
+        else
+            v[i] = make_uint4(0, 0, 0, 0);
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        m = fg_pk_max_u16(m, fg_pk_max_u16(fg_pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                                           fg_pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu)));
+    m = fg_row16_max_pk(m);
+    m = fg_pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 16));
+    m = fg_pk_max_u16(m, (uint32_t)__shfl_xor((int)m, 32));
+    if ((t & 63) == 0) wmax[t >> 6] = fg_max_halves(m);
+    __syncthreads();
+    uint32_t a = wmax[0] > wmax[1] ? wmax[0] : wmax[1];
+    uint32_t b = wmax[2] > wmax[3] ? wmax[2] : wmax[3];
+    const float s = fg_scale_from_amax_bits(a > b ? a : b, pow2);
+    if (t == 0) scales[blockIdx.y * kblocks + blockIdx.x] = s;
+    const fg_divisor d = fg_make_divisor(s);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int64_t r = r0 + rsub + 16 * i;
+        uint32_t lo = fg_cvt2<false>(fg_div(fg_bf16_lo(v[i].x), d), fg_div(fg_bf16_hi(v[i].x), d), 0);
+        lo = fg_cvt2<true>(fg_div(fg_bf16_lo(v[i].y), d), fg_div(fg_bf16_hi(v[i].y), d), lo);
+        uint32_t hi = fg_cvt2<false>(fg_div(fg_bf16_lo(v[i].z), d), fg_div(fg_bf16_hi(v[i].z), d), 0);
+        hi = fg_cvt2<true>(fg_div(fg_bf16_lo(v[i].w), d), fg_div(fg_bf16_hi(v[i].w), d), hi);
+        if (r < n) *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Host launchers (arguments already validated by the C-ABI layer).
+// ------------------------------------------------------------------------------------------------
+constexpr int kActColsUnroll = 4;
+
+hipError_t fg_launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
+                                    uint8_t* q, float* scales, hipStream_t stream) {
+    dim3 grid((unsigned)((rows + 16 * kActColsUnroll - 1) / (16 * kActColsUnroll)), (unsigned)(cols / FG_GROUP));
+    hipLaunchKernelGGL(fg_quant_act_cols_kernel<kActColsUnroll>, grid, dim3(256), 0, stream, x, rows, ld, pow2, q,
+                       cols, scales);
+    return hipGetLastError();
+}
+
+hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
+                                    uint8_t* q, float* scales, hipStream_t stream) {
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(rows / FG_GROUP));
+    hipLaunchKernelGGL(fg_quant_act_rows_kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, pow2, q, scales);
+    return hipGetLastError();
+}
+
+hipError_t fg_launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ld, int pow2, uint8_t* q,
+                             float* scales, hipStream_t stream) {
+    dim3 grid((unsigned)(k / FG_GROUP), (unsigned)((n + FG_GROUP - 1) / FG_GROUP));
+    hipLaunchKernelGGL(fg_quant_w_kernel, grid, dim3(256), 0, stream, w, n, ld, k / FG_GROUP, pow2, q, k, scales);
+    return hipGetLastError();
+}

@@ -1,0 +1,148 @@
+/*
+ * fp8fg — fine-grained FP8 (OCP E4M3) quantization and block-scaled GEMMs for MI355X (gfx950).
+ *
+ * C ABI. Every pointer argument is DEVICE memory owned by the caller; the library never allocates, frees
+ * or synchronises. All work is enqueued asynchronously on `stream` (0 = the null stream). The library keeps
+ * no state between calls and is safe to call from several threads. Arguments are checked on the host
+ * before any HIP call; a failed check returns a status and enqueues nothing. A launch failure returns
+ * FG_ERR_HIP and fg_last_hip_error() gives the hipError_t on the calling thread.
+ *
+ * Sources (web pages quoting the FP8 training section of the DeepSeek-V3 report):
+ *   [W1] "5 Ways You can get More Deepseek While Spending Less"
+ *   [W2] untitled page, why-be.why-be.co.kr board "as_center", post 65967
+ *   [W3] untitled page, cameseeing.com board "community", post 22576
+ *   [W4] "Three Fast Methods To Study Deepseek"
+ *   [W5] untitled page, gnrental.net board "free", post 15227
+ *
+ * Number formats.
+ *   bf16 inputs: IEEE bfloat16 bit patterns (2 bytes). Inputs must be finite (NaN/Inf: undefined result).
+ *   codes: OCP E4M3 ("E4M3FN"), 1 byte: bias 7, max 448 (0x7E), no infinities, 0x7F/0xFF are NaN
+ *          (E4M3 on all tensors: [W4]/[W5], the passage contrasting it with the hybrid E4M3/E5M2 format).
+ *   scales: fp32. Dequantized value = decode(code) * scale.
+ *
+ * Quantization rule (identical for every quantizer): for each group (1x128 tile or 128x128 block),
+ *   amax  = max |x| over the group, computed from the data being quantized ("online"; [W3], passage next
+ *           to Figure 7 (a));
+ *   scale = amax / 448 in fp32 (IEEE division): the max-abs is aligned to the largest E4M3 value ([W1],
+ *           passage on scaling the maximum absolute value to the maximum representable FP8 value);
+ *           amax == 0 gives scale 1; a scale below FLT_MIN is raised to FLT_MIN;
+ *           FG_SCALE_POW2 then rounds the scale up to the next integral power of two ([W1], opening
+ *           paragraph: scaling factors that are integral powers of 2);
+ *   code  = E4M3 round-to-nearest-even of the fp32 quotient x / scale (correctly rounded division).
+ *   Codes and scales are bit-exact against a plain CPU statement of this rule.
+ *
+ * GEMM rule ([W1]: per-group scaling factors along the inner dimension; partial sums promoted into FP32
+ * every 128 elements of K, the "128 elements, equal to four WGMMAs" interval; [W5]: GEMMs take FP8
+ * inputs and produce BF16 or FP32): for every output element and every 128-element block b of the
+ * contraction dimension, in ascending order,
+ *   P_b  = sum over the block of decode(a) * decode(b)          (matrix-core partial sum)
+ *   acc  = fma(P_b, scale_a * scale_b, acc)                     (FP32 promotion in registers)
+ * and the output is acc (FP32) or acc rounded to nearest-even BF16.
+ * The matrix core's summation inside a block is hardware-defined; results agree with the exact value to
+ * within a max relative error of 1e-3 (FP32 output) / 1e-2 (BF16 output), normwise.
+ *
+ * Layouts are row-major. "ld" arguments are row strides in elements.
+ * Activation scales are MN-major: scale[group][row] (rows contiguous), so one 128-deep K step of a GEMM
+ * reads its rows' scales as one contiguous run.
+ */
+#ifndef FP8FG_H
+#define FP8FG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FG_OK = 0,
+    FG_ERR_INVALID_ARG = 1,        /* null pointer, negative size, bad enum, ld smaller than the row   */
+    FG_ERR_UNSUPPORTED_SHAPE = 2,  /* a size that the operation's tiling requires to be a multiple    */
+    FG_ERR_MISALIGNED = 3,         /* a pointer or leading dimension breaks the 16-byte row alignment */
+    FG_ERR_HIP = 4                 /* the HIP runtime reported an error at launch                     */
+} fg_status;
+
+typedef enum { FG_SCALE_FP32 = 0, FG_SCALE_POW2 = 1 } fg_scale_mode;
+typedef enum { FG_OUT_F32 = 0, FG_OUT_BF16 = 1 } fg_out_dtype;
+typedef enum {
+    FG_ALONG_COLS = 0,   /* 1x128 tiles along the columns (per token, per 128 channels)               */
+    FG_ALONG_ROWS = 1    /* 1x128 tiles along the rows (per channel, per 128 tokens), codes transposed */
+} fg_tile_axis;
+
+/* 1x128 activation quantization ([W2]/[W3]/[W4], Figure 7 (a): activations are grouped and scaled per
+ * token per 128 channels; the forward activations are kept as 1x128 FP8 tiles for the backward pass,
+ * [W1] Figure 6 passage).
+ *
+ *   x       bf16 [rows][cols], row stride ld_x (elements).
+ *   FG_ALONG_COLS: requires cols % 128 == 0. Writes q u8 [rows][cols] (row stride cols) and
+ *                  scales f32 [cols/128][rows]. Any rows >= 0.
+ *   FG_ALONG_ROWS: the token-dimension tiling used by the weight-gradient GEMM, which contracts over
+ *                  tokens. Requires rows % 128 == 0 and cols % 8 == 0. Writes q u8 [cols][rows]
+ *                  (transposed, row stride rows) and scales f32 [rows/128][cols].
+ *   Alignment: x, q 16-byte aligned; ld_x % 8 == 0; scales 4-byte aligned.
+ *   rows == 0 or cols == 0 is a no-op returning FG_OK. */
+fg_status fg_quantize_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                fg_tile_axis axis, fg_scale_mode mode,
+                                uint8_t* q, float* scales, hipStream_t stream);
+
+/* 128x128 weight-block quantization ([W2]/[W3]/[W4], Figure 7 (a): per 128 input channels per 128
+ * output channels).
+ *   w       bf16 [n][k], row stride ld_w; k % 128 == 0; any n >= 0 (a short last block row-group takes
+ *           the max over the rows it has).
+ *   q       u8 [n][k] (row stride k);  scales f32 [ceil(n/128)][k/128] row-major.
+ *   Alignment: w, q 16-byte aligned; ld_w % 8 == 0. */
+fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_w,
+                                fg_scale_mode mode, uint8_t* q, float* scales, hipStream_t stream);
+
+/* Fprop ([W1]/[W3]/[W4]/[W5], Figure 6, forward pass): Y[M][N] = X[M][K] . W[N][K]^T.
+ *   xq u8 [M][K], sx f32 [K/128][M]   (from fg_quantize_act_1x128, FG_ALONG_COLS)
+ *   wq u8 [N][K], sw f32 [ceil(N/128)][K/128]   (from fg_quantize_w_128x128)
+ *   y  [M][N] f32 or bf16 (row stride N).  K % 128 == 0; any M, N >= 0 (M == 0 or N == 0: no-op;
+ *   K == 0 writes zeros). Pointers 16-byte aligned. */
+fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                            int64_t M, int64_t N, int64_t K, void* y, fg_out_dtype out,
+                            hipStream_t stream);
+
+/* Dgrad (Figure 6, activation backward pass): dX[M][K] = dY[M][N] . W[N][K], contracting over N.
+ *   dyq u8 [M][N], sdy f32 [N/128][M]   (dY quantized FG_ALONG_COLS)
+ *   wq  u8 [N][K], sw f32 [N/128][K/128] (the same codes and 128x128 block scales as Fprop; the block
+ *       is a 128-group along both axes, so it serves the transposed contraction unchanged; the kernel
+ *       reads W transposed on chip, the transposed read the pages ask of future hardware, [W5])
+ *   dx  [M][K] f32 or bf16.  N % 128 == 0, K % 128 == 0, any M. */
+fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
+                            int64_t M, int64_t N, int64_t K, void* dx, fg_out_dtype out,
+                            hipStream_t stream);
+
+/* Wgrad (Figure 6, weight backward pass): dW[N][K] (+)= dY[M][N]^T . X[M][K], contracting over the M
+ * tokens, from token-dimension quantized operands:
+ *   dytq u8 [N][M], sdyt f32 [M/128][N]   (dY quantized FG_ALONG_ROWS)
+ *   xtq  u8 [K][M], sxt  f32 [M/128][K]   (X quantized FG_ALONG_ROWS)
+ *   dw   f32 [N][K]; weight gradients stay FP32 ([W5], passage on master weights and gradients).
+ *        accumulate != 0: the FP32 accumulation of each element starts from the value already in dw.
+ *   M % 128 == 0; any N, K >= 0 with K % 4 == 0. */
+fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
+                            int64_t M, int64_t N, int64_t K, float* dw, int accumulate,
+                            hipStream_t stream);
+
+/* Grouped Fprop for the routed experts of one GPU ([W4]: MoE layers of 256 routed experts with expert
+ * intermediate dimension 2048, 8 active per token; [W5]: each GPU hosts 8 experts). For each group g:
+ *   Y[off[g]:off[g+1]][:] = X[off[g]:off[g+1]][:] . W[g]^T
+ *   xq u8 [T][K], sx f32 [K/128][T]; wq u8 [G][N][K], sw f32 [G][ceil(N/128)][K/128]; y [T][N].
+ *   d_offsets: DEVICE int32 [G+1], non-decreasing, d_offsets[0] == 0, d_offsets[G] == T (precondition,
+ *   not re-checked on the host). K % 128 == 0, G >= 1. */
+fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                              const int32_t* d_offsets, int32_t G, int64_t total_rows,
+                              int64_t N, int64_t K, void* y, fg_out_dtype out, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* fg_status_string(fg_status s);
+
+/* hipError_t (as int) of the most recent FG_ERR_HIP on the calling thread; 0 if none. */
+int fg_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8FG_H */

@@ -1,0 +1,94 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/fp8fg.h declares,
+and rejects bad arguments on the host with the documented status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_fine_grained_amax_amd as fg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8fg.h")
+
+OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
+A16 = 1 << 20          # fake, 16-byte aligned "device" addresses: never dereferenced on these paths
+A16B = 2 << 20
+ODD = (1 << 20) + 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fg_status|const char\*|int)\s+(fg_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fg.LIB_PATH):
+        from fp8_fine_grained_amax_amd import build
+        build.build()
+    return fg.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported shape"),
+                       (3, "misaligned pointer or leading dimension"), (4, "HIP runtime error")]:
+        assert fg.fg_status_string(code) == text
+    assert L.fg_last_hip_error() == 0
+
+
+def test_quantize_act_rejections(L):
+    q = L.fg_quantize_act_1x128
+    assert q(A16, -1, 128, 128, 0, 0, A16, A16, None) == INVALID           # negative rows
+    assert q(A16, 4, 128, 128, 2, 0, A16, A16, None) == INVALID            # bad axis
+    assert q(A16, 4, 128, 128, 0, 5, A16, A16, None) == INVALID            # bad mode
+    assert q(A16, 4, 128, 64, 0, 0, A16, A16, None) == INVALID             # ld < cols
+    assert q(None, 4, 128, 128, 0, 0, A16, A16, None) == INVALID           # null input
+    assert q(A16, 4, 100, 104, 0, 0, A16, A16, None) == SHAPE              # cols % 128 (along cols)
+    assert q(A16, 100, 64, 64, 1, 0, A16, A16, None) == SHAPE              # rows % 128 (along rows)
+    assert q(A16, 128, 60, 64, 1, 0, A16, A16, None) == SHAPE              # cols % 8 (along rows)
+    assert q(ODD, 4, 128, 128, 0, 0, A16, A16, None) == MISALIGNED         # x not 16 B aligned
+    assert q(A16, 4, 128, 132, 0, 0, A16, A16, None) == MISALIGNED         # ld % 8
+    assert q(A16, 0, 128, 128, 0, 0, None, None, None) == OK               # empty: no-op
+
+
+def test_quantize_w_rejections(L):
+    q = L.fg_quantize_w_128x128
+    assert q(A16, 128, 100, 100, 0, A16, A16, None) == SHAPE               # k % 128
+    assert q(A16, 128, 128, 128, 3, A16, A16, None) == INVALID             # bad mode
+    assert q(A16, 128, 128, 128, 0, ODD, A16, None) == MISALIGNED
+    assert q(A16, 0, 128, 128, 0, None, None, None) == OK
+
+
+def test_gemm_rejections(L):
+    f = L.fg_fp8_gemm_fprop
+    assert f(A16, A16, A16, A16, 128, 128, 100, A16, 0, None) == SHAPE     # K % 128
+    assert f(A16, A16, A16, A16, 128, 128, 128, A16, 7, None) == INVALID   # bad out dtype
+    assert f(A16, A16, None, A16, 128, 128, 128, A16, 0, None) == INVALID  # null W
+    assert f(A16, A16, A16, A16, 128, 128, 128, ODD, 0, None) == MISALIGNED
+    assert f(None, None, None, None, 0, 128, 128, None, 0, None) == OK     # empty
+    d = L.fg_fp8_gemm_dgrad
+    assert d(A16, A16, A16, A16, 128, 200, 128, A16, 0, None) == SHAPE     # N (contraction) % 128
+    assert d(A16, A16, A16, A16, 128, 256, 200, A16, 0, None) == SHAPE     # K % 128
+    w = L.fg_fp8_gemm_wgrad
+    assert w(A16, A16, A16, A16, 100, 128, 128, A16, 0, None) == SHAPE     # M (tokens) % 128
+    assert w(A16, A16, A16, A16, 128, 128, 130, A16, 0, None) == SHAPE     # K % 4
+    assert w(A16, A16, A16, ODD, 128, 128, 128, A16, 0, None) == MISALIGNED  # per-row scales need 16 B
+    g = L.fg_fp8_grouped_gemm
+    assert g(A16, A16, A16, A16, A16B, 0, 128, 128, 128, A16, 0, None) == INVALID   # G < 1
+    assert g(A16, A16, A16, A16, None, 2, 128, 128, 128, A16, 0, None) == INVALID   # null offsets
+    assert g(A16, A16, A16, A16, A16B, 2, 128, 128, 100, A16, 0, None) == SHAPE     # K % 128
+    assert L.fg_last_hip_error() == 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(fg.Fp8fgError):
+        fg.fg_quantize_act_1x128(torch.zeros(4, 128, dtype=torch.bfloat16))

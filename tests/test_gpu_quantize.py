@@ -1,0 +1,174 @@
+"""GPU parity: the HIP quantizers against the CPU oracle, bit-exact on codes and scales.
+
+Workloads are the seeded synthetic inputs (full sizes of the DeepSeek-V3-like Linear and its backward
+pair, the MoE share, the tiny case) plus edge cases: ragged rows/columns, padded row strides, zero and
+subnormal tiles, signed zeros, bf16 extremes, tiny scales, and a sweep over every finite bf16 value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_fine_grained_amax_amd as fg
+import oracle
+from fp8_fine_grained_amax_amd import workloads as wl
+from tests.gpu_util import bits, device, np_u8, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_act(x_cpu, axis, pow2, ld_pad=0):
+    xb = bits(x_cpu)
+    x = to_dev(x_cpu)
+    if ld_pad:
+        big = torch.zeros((x.shape[0], x.shape[1] + ld_pad), dtype=torch.bfloat16, device=x.device)
+        big[:, : x.shape[1]] = x
+        x = big[:, : x_cpu.shape[1]]
+    q, s = fg.fg_quantize_act_1x128(x, axis=axis, pow2=pow2)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_act_1x128(xb, axis, pow2)
+    q_gpu, s_gpu = np_u8(q), s.cpu().numpy()
+    assert np.array_equal(s_gpu.view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+    bad = np.argwhere(q_gpu != q_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+def _check_w(w_cpu, pow2):
+    q, s = fg.fg_quantize_w_128x128(to_dev(w_cpu), pow2=pow2)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_w_128x128(bits(w_cpu), pow2)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+    assert np.array_equal(np_u8(q), q_ref), "codes differ"
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_tiny_config(pow2):
+    device()
+    x, w = wl.tiny_fprop()
+    _check_act(x, fg.FG_ALONG_COLS, pow2)
+    _check_w(w, pow2)
+
+
+@pytest.fixture(scope="module")
+def dsv3():
+    device()
+    x, w = wl.dsv3_fprop()
+    dy = wl.dsv3_backward_dy()
+    return x, w, dy
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_dsv3_activation_rowwise(dsv3, pow2):
+    _check_act(dsv3[0], fg.FG_ALONG_COLS, pow2)
+
+
+def test_dsv3_weight_blocks(dsv3):
+    _check_w(dsv3[1], False)
+
+
+def test_dsv3_weight_blocks_pow2(dsv3):
+    _check_w(dsv3[1], True)
+
+
+def test_dsv3_backward_dy_rowwise(dsv3):
+    _check_act(dsv3[2], fg.FG_ALONG_COLS, False)
+
+
+def test_dsv3_backward_token_dim(dsv3):
+    _check_act(dsv3[2], fg.FG_ALONG_ROWS, False)      # dY^T for Wgrad
+    _check_act(dsv3[0], fg.FG_ALONG_ROWS, False)      # X^T for Wgrad
+
+
+def test_moe_share_inputs():
+    device()
+    d = wl.moe_inputs(rows_scale=0.125)
+    _check_act(d["x"], fg.FG_ALONG_COLS, False)
+    _check_act(d["h"], fg.FG_ALONG_COLS, True)
+    _check_w(d["w_up"][0], False)
+    _check_w(d["w_down"][3], False)
+
+
+@pytest.mark.parametrize("rows,cols,ld_pad", [(1, 128, 0), (37, 384, 8), (65, 1024, 0), (1000, 256, 24)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_rowwise_ragged_and_strided(rows, cols, ld_pad, pow2):
+    device()
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = wl.normal_bf16(rng, (rows, cols), 3.0, outlier_channels=2, outlier_scale=100.0)
+    _check_act(x, fg.FG_ALONG_COLS, pow2, ld_pad)
+
+
+@pytest.mark.parametrize("rows,cols,ld_pad", [(128, 8, 0), (256, 200, 8), (384, 72, 0), (128, 1032, 16)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_token_dim_ragged_and_strided(rows, cols, ld_pad, pow2):
+    device()
+    rng = np.random.default_rng(rows + cols * 3)
+    x = wl.normal_bf16(rng, (rows, cols), 0.5, outlier_channels=1, outlier_scale=50.0)
+    _check_act(x, fg.FG_ALONG_ROWS, pow2, ld_pad)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (300, 256), (129, 640)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_weight_ragged(n, k, pow2):
+    device()
+    rng = np.random.default_rng(n + k)
+    _check_w(wl.normal_bf16(rng, (n, k), 0.02), pow2)
+
+
+def _special_tiles():
+    """Rows of 128 bf16 values exercising the scale and rounding edge cases."""
+    rows = []
+    z = np.zeros(128, np.uint16)
+    rows.append(z.copy())                                           # all +0: scale 1
+    r = z.copy(); r[::2] = 0x8000; rows.append(r)                   # mix of -0 and +0
+    r = z.copy(); r[5] = 0x0001; r[9] = 0x8003; rows.append(r)      # bf16 subnormals only (tiny scale)
+    r = z.copy(); r[0] = 0x7F7F; r[1] = 0xFF7F; r[2] = 0x0001; rows.append(r)   # bf16 max and min
+    r = z.copy(); r[0] = 0x0080; r[1] = 0x8080; r[2] = 0x0001; rows.append(r)   # FLT_MIN-sized amax
+    r = z.copy(); r[0] = 0x43E0; r[1:8] = [0x3A80, 0x3AC0, 0x3B40, 0x3B00, 0xBA80, 0x8000, 0x3F80]; rows.append(r)  # 448 & ties
+    r = z.copy(); r[:] = 0x3F80; rows.append(r)                      # constant tile
+    r = z.copy(); r[0] = 0x11E0; r[1] = 0x1100; r[2] = 0x9180; rows.append(r)   # amax = 448 * 2^-100: s = 2^-100
+    r = z.copy(); r[0] = 0x11DF; r[1] = 0x0080; r[2] = 0x8C00; r[3] = 0x0001; rows.append(r)  # s just below 2^-100
+    r = z.copy(); r[0] = 0x0D00; r[1] = 0x0080; r[2] = 0x8C00; rows.append(r)   # s < 2^-100 (pre-scaled path)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_special_value_tiles(pow2):
+    device()
+    t = _special_tiles()
+    x = torch.from_numpy(t.view(np.int16)).view(torch.bfloat16)
+    _check_act(x, fg.FG_ALONG_COLS, pow2)
+
+
+def test_special_value_tiles_token_dim_padded():
+    device()
+    t = _special_tiles()
+    pad = np.zeros((16, 128), np.uint16)
+    pad[: t.shape[0]] = t
+    xt = torch.from_numpy(np.ascontiguousarray(pad.T).view(np.int16)).view(torch.bfloat16)
+    for pow2 in (False, True):
+        _check_act(xt, fg.FG_ALONG_ROWS, pow2)
+        _check_w(torch.from_numpy(pad.view(np.int16)).view(torch.bfloat16), pow2)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_every_finite_bf16_value(pow2):
+    """Each finite bf16 pattern appears once, in tiles of 128 consecutive patterns (so tile max-abs
+    values span the whole exponent range), and again in tiles whose max-abs is fixed at 448 * 2^j."""
+    device()
+    allb = np.arange(65536, dtype=np.uint32)
+    finite = allb[((allb >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    n = (finite.size // 128) * 128
+    a = finite[:n].reshape(-1, 128)
+    rng = np.random.default_rng(3)
+    b = rng.permutation(finite)[:n].reshape(-1, 128).copy()
+    b[:, 0] = np.where(np.arange(b.shape[0]) % 2 == 0, 0x43E0, 0x7F00)        # 448 or 2^127 max
+    x = np.concatenate([a, b])
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    _check_act(xt, fg.FG_ALONG_COLS, pow2)
+    _check_act(xt[:, :128].contiguous()[: (x.shape[0] // 128) * 128], fg.FG_ALONG_ROWS, pow2)
+
+
+def test_deterministic_repeat(dsv3):
+    x = to_dev(dsv3[0])
+    q1, s1 = fg.fg_quantize_act_1x128(x)
+    q2, s2 = fg.fg_quantize_act_1x128(x)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
