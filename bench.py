@@ -1,0 +1,305 @@
+"""Benchmark: fine-grained FP8 Linear training pass on one MI355X.
+
+One step = the whole hot path over one batch of the DeepSeek-V3-like dense MLP Linear
+(X [4096, 7168], W [18432, 7168], dY [4096, 18432], seeded synthetic bf16):
+  forward : quantize X (1x128 along channels), quantize W (128x128 blocks), Fprop  Y = X W^T (BF16 out)
+  backward: quantize dY (1x128 along channels), Dgrad dX = dY W (FP32 out),
+            quantize dY and X (1x128 along tokens, transposed), Wgrad dW = dY^T X (FP32 out)
+`value` is the FP8 GEMM throughput of the whole step (3 x 2MNK FLOP over the step's wall time), with
+all inputs resident in HBM when the timed region starts. Per-kernel times come from HIP events on the
+stream the kernels run on. Also reported: per-kernel roofline fractions, cold-cache quantize bandwidth
+(a 1 GiB scrub between launches defeats the 256 MB Infinity Cache), the grouped MoE GEMM on one GPU's
+expert share, and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-moe] [--no-cpu] [--calib-copy]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 GEMM TFLOPS (% of dense FP8 peak) + quantize GB/s, 1 MI355X"
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "quant.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "fp8_fine_grained_amax_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def quant_bytes(rows, cols):
+    """Algorithmic HBM bytes of a 1x128 / 128x128 quantization: 2 B in + 1 B out per element,
+    4 B per scale (one per 128 or per 16384 elements)."""
+    return rows * cols * 3 + rows * cols // 128 * 4
+
+
+def quant_w_bytes(n, k):
+    return n * k * 3 + (n // 128) * (k // 128) * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true", help="only run a 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    if args.calib_copy:
+        n = 512 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+
+    import fp8_fine_grained_amax_amd as fg
+    from fp8_fine_grained_amax_amd import workloads as wl
+
+    fg.lib()
+    stream = torch.cuda.current_stream(dev)
+    shape = wl.DSV3_MLP
+    M, N, K = shape.M, shape.N, shape.K
+
+    t_gen = time.time()
+    x_c, w_c = wl.dsv3_fprop()
+    dy_c = wl.dsv3_backward_dy()
+    x, w, dy = x_c.to(dev), w_c.to(dev), dy_c.to(dev)
+    gen_s = time.time() - t_gen
+    print(f"[bench] inputs ready ({gen_s:.1f}s): X {tuple(x.shape)} W {tuple(w.shape)} dY {tuple(dy.shape)}",
+          file=sys.stderr, flush=True)
+
+    u8, f32 = torch.uint8, torch.float32
+    bufs = dict(
+        xq=torch.empty((M, K), dtype=u8, device=dev), sx=torch.empty((K // 128, M), dtype=f32, device=dev),
+        wq=torch.empty((N, K), dtype=u8, device=dev), sw=torch.empty((N // 128, K // 128), dtype=f32, device=dev),
+        y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        dyq=torch.empty((M, N), dtype=u8, device=dev), sdy=torch.empty((N // 128, M), dtype=f32, device=dev),
+        dx=torch.empty((M, K), dtype=f32, device=dev),
+        dytq=torch.empty((N, M), dtype=u8, device=dev), sdyt=torch.empty((M // 128, N), dtype=f32, device=dev),
+        xtq=torch.empty((K, M), dtype=u8, device=dev), sxt=torch.empty((M // 128, K), dtype=f32, device=dev),
+        dw=torch.empty((N, K), dtype=f32, device=dev),
+    )
+    B = bufs
+    ops = [
+        ("quant_x_rowwise", lambda: fg.fg_quantize_act_1x128(x, q=B["xq"], scales=B["sx"]),
+         "hbm", quant_bytes(M, K)),
+        ("quant_w_128x128", lambda: fg.fg_quantize_w_128x128(w, q=B["wq"], scales=B["sw"]),
+         "hbm", quant_w_bytes(N, K)),
+        ("fprop", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"]),
+         "mfma", 2.0 * M * N * K),
+        ("quant_dy_rowwise", lambda: fg.fg_quantize_act_1x128(dy, q=B["dyq"], scales=B["sdy"]),
+         "hbm", quant_bytes(M, N)),
+        ("dgrad", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"]),
+         "mfma", 2.0 * M * N * K),
+        ("quant_dy_tokendim", lambda: fg.fg_quantize_act_1x128(dy, axis=fg.FG_ALONG_ROWS, q=B["dytq"], scales=B["sdyt"]),
+         "hbm", quant_bytes(M, N)),
+        ("quant_x_tokendim", lambda: fg.fg_quantize_act_1x128(x, axis=fg.FG_ALONG_ROWS, q=B["xtq"], scales=B["sxt"]),
+         "hbm", quant_bytes(M, K)),
+        ("wgrad", lambda: fg.fg_fp8_gemm_wgrad(B["dytq"], B["sdyt"], B["xtq"], B["sxt"], dw=B["dw"]),
+         "mfma", 2.0 * M * N * K),
+    ]
+
+    def run_step(events=None):
+        for i, (_, fn, _, _) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(ev[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kernel_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+                     for i, (name, _, _, _) in enumerate(ops)}
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    gemm_flop = 3 * 2.0 * M * N * K
+    value = gemm_flop / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    for name, _, bound, work in ops:
+        ms = per_kernel_ms[name]
+        if bound == "mfma":
+            ach = work / (ms * 1e-3) / 1e12
+            kernels[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4)}
+        else:
+            ach = work / (ms * 1e-3) / 1e9
+            kernels[name] = {"ms": round(ms, 4), "GB/s": round(ach, 1), "frac_hbm_peak": round(ach / PEAK_HBM_GBPS, 4)}
+
+    # Cold-cache quantize bandwidth: scrub 1 GiB before each launch (outside the timed event pair).
+    cold = {}
+    if not args.no_cold:
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for name, fn, bound, work in ops:
+            if bound != "hbm":
+                continue
+            times = []
+            for _ in range(5):
+                scrub.fill_(0)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            gbps = work / (ms * 1e-3) / 1e9
+            cold[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        del scrub
+        print("[bench] cold-cache quantize timings done", file=sys.stderr, flush=True)
+
+    # Grouped MoE GEMM (one GPU's expert share): up-projection then down-projection, BF16 out.
+    moe = None
+    if not args.no_moe:
+        del x, w, dy, bufs, B
+        d = wl.moe_inputs()
+        T = int(d["offsets"][-1])
+        E, I, H = wl.MOE_EXPERTS, wl.MOE_INTER, wl.MOE_HIDDEN
+        xm, hm = d["x"].to(dev), d["h"].to(dev)
+        wu, wd = d["w_up"].to(dev), d["w_down"].to(dev)
+        off = torch.from_numpy(d["offsets"]).to(dev)
+        xq, sx = fg.fg_quantize_act_1x128(xm)
+        hq, sh = fg.fg_quantize_act_1x128(hm)
+        wuq = torch.empty((E, I, H), dtype=u8, device=dev)
+        wus = torch.empty((E, I // 128, H // 128), dtype=f32, device=dev)
+        wdq = torch.empty((E, H, I), dtype=u8, device=dev)
+        wds = torch.empty((E, H // 128, I // 128), dtype=f32, device=dev)
+        for e in range(E):
+            fg.fg_quantize_w_128x128(wu[e], q=wuq[e], scales=wus[e])
+            fg.fg_quantize_w_128x128(wd[e], q=wdq[e], scales=wds[e])
+        yu = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        res = {}
+        for name, fn, flop in [
+            ("grouped_up", lambda: fg.fg_fp8_grouped_gemm(xq, sx, wuq, wus, off, y=yu), 2.0 * T * I * H),
+            ("grouped_down", lambda: fg.fg_fp8_grouped_gemm(hq, sh, wdq, wds, off, y=yd), 2.0 * T * I * H),
+            ("quant_moe_x_rowwise", lambda: fg.fg_quantize_act_1x128(xm, q=xq, scales=sx), None),
+        ]:
+            for _ in range(3):
+                fn()
+            times = []
+            for _ in range(10):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            if flop is not None:
+                ach = flop / (ms * 1e-3) / 1e12
+                res[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4)}
+            else:
+                gbps = quant_bytes(T, H) / (ms * 1e-3) / 1e9
+                res[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        moe = {"workload": "moe_grouped_8experts_65536rows_hidden7168_inter2048", "rows_per_expert": d["rows"].tolist(), **res}
+        print("[bench] grouped MoE timings done", file=sys.stderr, flush=True)
+
+    # Roofline of the dominant (longest) GEMM kernel of the step.
+    gemm_names = [n for n, _, b, _ in ops if b == "mfma"]
+    dom = max(gemm_names, key=lambda n: per_kernel_ms[n])
+    ach = 2.0 * M * N * K / (per_kernel_ms[dom] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("kernel_source_hash") == kernel_source_hash() and dom in tr.get("bytes_per_launch", {}):
+                traffic = tr["bytes_per_launch"][dom]
+        except (OSError, ValueError):
+            traffic = None
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline()
+
+    qnames = [n for n, _, b, _ in ops if b == "hbm"]
+    qbytes = sum(wk for n, _, b, wk in ops if b == "hbm")
+    qms = sum(per_kernel_ms[n] for n in qnames)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "dsv3_dense_mlp_linear_fwd_bwd", "M_tokens": M, "N_out": N, "K_in": K,
+                   "tiles": "1x128 activations, 128x128 weights", "scale_mode": "fp32", "accumulate": "fp32, promoted every 128 K",
+                   "fprop_out": "bf16", "dgrad_out": "f32", "wgrad_out": "f32"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "quantize_GBps_in_step": round(qbytes / (qms * 1e-3) / 1e9, 1),
+        "kernels": kernels,
+        "quantize_cold_cache": cold,
+        "moe_grouped": moe,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline():
+    """The oracle as it stands, on a bounded sample of the step's GEMM work (sampled outputs of Fprop,
+    Dgrad and Wgrad at the full shapes, each a full 128-blocked promoted dot product), run for ~10-20 s
+    on the host's cores. Reported in the same unit as `value`."""
+    import numpy as np
+    import oracle
+    from fp8_fine_grained_amax_amd import workloads as wl
+
+    shape = wl.DSV3_MLP
+    M, N, K = shape.M, shape.N, shape.K
+    rng = np.random.default_rng(99)
+    # codes and scales with the workload's value ranges (the oracle's GEMM cost does not depend on them)
+    xq = rng.integers(0, 0x7E, (M, K), dtype=np.uint8)
+    wq = rng.integers(0, 0x7E, (N, K), dtype=np.uint8)
+    sx = rng.uniform(1e-3, 1e-2, (K // 128, M)).astype(np.float32)
+    sw = rng.uniform(1e-5, 1e-4, (N // 128, K // 128)).astype(np.float32)
+    npts, total_flop, elapsed = 256, 0.0, 0.0
+    while elapsed < 10.0 and npts <= 1 << 22:
+        pts = rng.integers(0, M * N, npts, dtype=np.int64)
+        t = time.perf_counter()
+        oracle.gemm_fprop(xq, sx, wq, sw, out_bf16=True, pts=pts, want_exact=False)
+        dt = time.perf_counter() - t
+        elapsed += dt
+        total_flop += 2.0 * K * npts
+        npts *= 2
+    value = total_flop / elapsed / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{int(total_flop / (2 * K))} sampled Fprop outputs of the 4096x18432x7168 GEMM "
+                      f"(each a 7168-deep promoted dot product), {elapsed:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
