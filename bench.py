@@ -54,6 +54,8 @@ def main():
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--pow2", action="store_true", help="power-of-2 scales (quantizers round scales up to 2^k; "
+                    "the GEMMs then apply them in the matrix core)")
     ap.add_argument("--calib-copy", action="store_true", help="only run a 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -103,22 +105,25 @@ def main():
         dw=torch.empty((N, K), dtype=f32, device=dev),
     )
     B = bufs
+    POW2 = bool(args.pow2)
     ops = [
-        ("quant_x_rowwise", lambda: fg.fg_quantize_act_1x128(x, q=B["xq"], scales=B["sx"]),
+        ("quant_x_rowwise", lambda: fg.fg_quantize_act_1x128(x, q=B["xq"], scales=B["sx"], pow2=POW2),
          "hbm", quant_bytes(M, K)),
-        ("quant_w_128x128", lambda: fg.fg_quantize_w_128x128(w, q=B["wq"], scales=B["sw"]),
+        ("quant_w_128x128", lambda: fg.fg_quantize_w_128x128(w, q=B["wq"], scales=B["sw"], pow2=POW2),
          "hbm", quant_w_bytes(N, K)),
-        ("fprop", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"]),
+        ("fprop", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=POW2),
          "mfma", 2.0 * M * N * K),
-        ("quant_dy_rowwise", lambda: fg.fg_quantize_act_1x128(dy, q=B["dyq"], scales=B["sdy"]),
+        ("quant_dy_rowwise", lambda: fg.fg_quantize_act_1x128(dy, q=B["dyq"], scales=B["sdy"], pow2=POW2),
          "hbm", quant_bytes(M, N)),
-        ("dgrad", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"]),
+        ("dgrad", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"], pow2=POW2),
          "mfma", 2.0 * M * N * K),
-        ("quant_dy_tokendim", lambda: fg.fg_quantize_act_1x128(dy, axis=fg.FG_ALONG_ROWS, q=B["dytq"], scales=B["sdyt"]),
+        ("quant_dy_tokendim", lambda: fg.fg_quantize_act_1x128(dy, axis=fg.FG_ALONG_ROWS, q=B["dytq"], scales=B["sdyt"],
+                                                               pow2=POW2),
          "hbm", quant_bytes(M, N)),
-        ("quant_x_tokendim", lambda: fg.fg_quantize_act_1x128(x, axis=fg.FG_ALONG_ROWS, q=B["xtq"], scales=B["sxt"]),
+        ("quant_x_tokendim", lambda: fg.fg_quantize_act_1x128(x, axis=fg.FG_ALONG_ROWS, q=B["xtq"], scales=B["sxt"],
+                                                              pow2=POW2),
          "hbm", quant_bytes(M, K)),
-        ("wgrad", lambda: fg.fg_fp8_gemm_wgrad(B["dytq"], B["sdyt"], B["xtq"], B["sxt"], dw=B["dw"]),
+        ("wgrad", lambda: fg.fg_fp8_gemm_wgrad(B["dytq"], B["sdyt"], B["xtq"], B["sxt"], dw=B["dw"], pow2=POW2),
          "mfma", 2.0 * M * N * K),
     ]
 
@@ -193,22 +198,22 @@ def main():
         xm, hm = d["x"].to(dev), d["h"].to(dev)
         wu, wd = d["w_up"].to(dev), d["w_down"].to(dev)
         off = torch.from_numpy(d["offsets"]).to(dev)
-        xq, sx = fg.fg_quantize_act_1x128(xm)
-        hq, sh = fg.fg_quantize_act_1x128(hm)
+        xq, sx = fg.fg_quantize_act_1x128(xm, pow2=POW2)
+        hq, sh = fg.fg_quantize_act_1x128(hm, pow2=POW2)
         wuq = torch.empty((E, I, H), dtype=u8, device=dev)
         wus = torch.empty((E, I // 128, H // 128), dtype=f32, device=dev)
         wdq = torch.empty((E, H, I), dtype=u8, device=dev)
         wds = torch.empty((E, H // 128, I // 128), dtype=f32, device=dev)
         for e in range(E):
-            fg.fg_quantize_w_128x128(wu[e], q=wuq[e], scales=wus[e])
-            fg.fg_quantize_w_128x128(wd[e], q=wdq[e], scales=wds[e])
+            fg.fg_quantize_w_128x128(wu[e], q=wuq[e], scales=wus[e], pow2=POW2)
+            fg.fg_quantize_w_128x128(wd[e], q=wdq[e], scales=wds[e], pow2=POW2)
         yu = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
         yd = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         res = {}
         for name, fn, flop in [
-            ("grouped_up", lambda: fg.fg_fp8_grouped_gemm(xq, sx, wuq, wus, off, y=yu), 2.0 * T * I * H),
-            ("grouped_down", lambda: fg.fg_fp8_grouped_gemm(hq, sh, wdq, wds, off, y=yd), 2.0 * T * I * H),
-            ("quant_moe_x_rowwise", lambda: fg.fg_quantize_act_1x128(xm, q=xq, scales=sx), None),
+            ("grouped_up", lambda: fg.fg_fp8_grouped_gemm(xq, sx, wuq, wus, off, y=yu, pow2=POW2), 2.0 * T * I * H),
+            ("grouped_down", lambda: fg.fg_fp8_grouped_gemm(hq, sh, wdq, wds, off, y=yd, pow2=POW2), 2.0 * T * I * H),
+            ("quant_moe_x_rowwise", lambda: fg.fg_quantize_act_1x128(xm, q=xq, scales=sx, pow2=POW2), None),
         ]:
             for _ in range(3):
                 fn()
@@ -257,7 +262,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": "dsv3_dense_mlp_linear_fwd_bwd", "M_tokens": M, "N_out": N, "K_in": K,
-                   "tiles": "1x128 activations, 128x128 weights", "scale_mode": "fp32", "accumulate": "fp32, promoted every 128 K",
+                   "tiles": "1x128 activations, 128x128 weights", "scale_mode": "pow2" if POW2 else "fp32", "accumulate": "fp32, promoted every 128 K",
                    "fprop_out": "bf16", "dgrad_out": "f32", "wgrad_out": "f32"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -34,10 +34,10 @@ def lib():
         P, I64, I, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int32
         L.fg_quantize_act_1x128.argtypes = [P, I64, I64, I64, I, I, P, P, P]
         L.fg_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P, P]
-        L.fg_fp8_gemm_fprop.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
-        L.fg_fp8_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
-        L.fg_fp8_gemm_wgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
-        L.fg_fp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, P]
+        L.fg_fp8_gemm_fprop.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
+        L.fg_fp8_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
+        L.fg_fp8_gemm_wgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
+        L.fg_fp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         for f in ("fg_quantize_act_1x128", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop", "fg_fp8_gemm_dgrad",
                   "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm"):
             getattr(L, f).restype = I
@@ -120,19 +120,23 @@ def fg_quantize_w_128x128(w, pow2: bool = False, q=None, scales=None):
     return q, scales
 
 
-def fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None):
-    """Y [M, N] = X [M, K] . W [N, K]^T from E4M3 codes and their scales."""
+def _mode(pow2):
+    return FG_SCALE_POW2 if pow2 else FG_SCALE_FP32
+
+
+def fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None, pow2: bool = False):
+    """Y [M, N] = X [M, K] . W [N, K]^T from E4M3 codes and their scales (pow2: all scales are powers of two)."""
     _gpu(xq, sx, wq, sw, y)
     M, K = xq.shape
     N = wq.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     _check(lib().fg_fp8_gemm_fprop(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _out_code(y.dtype),
-                                   _stream(xq.device)), "fg_fp8_gemm_fprop")
+                                   _mode(pow2), _stream(xq.device)), "fg_fp8_gemm_fprop")
     return y
 
 
-def fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.float32, dx=None):
+def fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.float32, dx=None, pow2: bool = False):
     """dX [M, K] = dY [M, N] . W [N, K], contracting over N, with W's codes and 128x128 block scales."""
     _gpu(dyq, sdy, wq, sw, dx)
     M, N = dyq.shape
@@ -140,11 +144,11 @@ def fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.float32, dx=None):
     if dx is None:
         dx = torch.empty((M, K), dtype=out_dtype, device=dyq.device)
     _check(lib().fg_fp8_gemm_dgrad(_ptr(dyq), _ptr(sdy), _ptr(wq), _ptr(sw), M, N, K, _ptr(dx), _out_code(dx.dtype),
-                                   _stream(dyq.device)), "fg_fp8_gemm_dgrad")
+                                   _mode(pow2), _stream(dyq.device)), "fg_fp8_gemm_dgrad")
     return dx
 
 
-def fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False):
+def fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False, pow2: bool = False):
     """dW [N, K] (+)= dY^T . X from token-dim quantized dYt [N, M] and Xt [K, M]; fp32 output."""
     _gpu(dytq, sdyt, xtq, sxt, dw)
     N, M = dytq.shape
@@ -154,11 +158,11 @@ def fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False):
             raise Fp8fgError("accumulate needs an existing dw")
         dw = torch.empty((N, K), dtype=torch.float32, device=dytq.device)
     _check(lib().fg_fp8_gemm_wgrad(_ptr(dytq), _ptr(sdyt), _ptr(xtq), _ptr(sxt), M, N, K, _ptr(dw), int(bool(accumulate)),
-                                   _stream(dytq.device)), "fg_fp8_gemm_wgrad")
+                                   _mode(pow2), _stream(dytq.device)), "fg_fp8_gemm_wgrad")
     return dw
 
 
-def fg_fp8_grouped_gemm(xq, sx, wq, sw, offsets, out_dtype=torch.bfloat16, y=None):
+def fg_fp8_grouped_gemm(xq, sx, wq, sw, offsets, out_dtype=torch.bfloat16, y=None, pow2: bool = False):
     """Per group g: Y[off[g]:off[g+1]] = X[off[g]:off[g+1]] . W[g]^T. offsets: device int32 [G+1]."""
     _gpu(xq, sx, wq, sw, offsets, y)
     if offsets.dtype != torch.int32:
@@ -168,5 +172,5 @@ def fg_fp8_grouped_gemm(xq, sx, wq, sw, offsets, out_dtype=torch.bfloat16, y=Non
     if y is None:
         y = torch.empty((T, N), dtype=out_dtype, device=xq.device)
     _check(lib().fg_fp8_grouped_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(offsets), G, T, N, K, _ptr(y),
-                                     _out_code(y.dtype), _stream(xq.device)), "fg_fp8_grouped_gemm")
+                                     _out_code(y.dtype), _mode(pow2), _stream(xq.device)), "fg_fp8_grouped_gemm")
     return y

@@ -12,14 +12,14 @@ hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t col
 hipError_t fg_launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ld, int pow2, uint8_t* q,
                              float* scales, hipStream_t stream);
 hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
-                                int64_t N, int64_t K, void* y, int out_bf16, hipStream_t stream);
+                                int64_t N, int64_t K, void* y, int out_bf16, int pow2, hipStream_t stream);
 hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
-                                int64_t N, int64_t K, void* dx, int out_bf16, hipStream_t stream);
+                                int64_t N, int64_t K, void* dx, int out_bf16, int pow2, hipStream_t stream);
 hipError_t fg_launch_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
-                                int64_t M, int64_t N, int64_t K, float* dw, int accumulate, hipStream_t stream);
+                                int64_t M, int64_t N, int64_t K, float* dw, int accumulate, int pow2, hipStream_t stream);
 hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                                   const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, void* y,
-                                  int out_bf16, hipStream_t stream);
+                                  int out_bf16, int pow2, hipStream_t stream);
 
 namespace {
 
@@ -43,7 +43,7 @@ fg_status from_hip(hipError_t e) {
 bool valid_mode(int m) { return m == FG_SCALE_FP32 || m == FG_SCALE_POW2; }
 bool valid_out(int o) { return o == FG_OUT_F32 || o == FG_OUT_BF16; }
 
-int64_t tiles(int64_t a, int64_t b) { return ((a + 255) / 256) * ((b + 255) / 256); }
+int64_t tiles(int64_t a, int64_t b) { return ((a + 255) / 256) * ((b + 127) / 128); }
 
 }  // namespace
 
@@ -93,48 +93,49 @@ fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_
 }
 
 fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
-                            int64_t N, int64_t K, void* y, fg_out_dtype out, hipStream_t stream) {
-    if (M < 0 || N < 0 || K < 0 || !valid_out(out)) return FG_ERR_INVALID_ARG;
+                            int64_t N, int64_t K, void* y, fg_out_dtype out, fg_scale_mode scales, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || !valid_out(out) || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return FG_OK;
     if (!y || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
     if (K % 128 != 0 || tiles(M, N) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw)) return FG_ERR_MISALIGNED;
-    return from_hip(fg_launch_gemm_fprop(xq, sx, wq, sw, M, N, K, y, out == FG_OUT_BF16, stream));
+    return from_hip(fg_launch_gemm_fprop(xq, sx, wq, sw, M, N, K, y, out == FG_OUT_BF16, scales == FG_SCALE_POW2, stream));
 }
 
 fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
-                            int64_t N, int64_t K, void* dx, fg_out_dtype out, hipStream_t stream) {
-    if (M < 0 || N < 0 || K < 0 || !valid_out(out)) return FG_ERR_INVALID_ARG;
+                            int64_t N, int64_t K, void* dx, fg_out_dtype out, fg_scale_mode scales, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || !valid_out(out) || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
     if (M == 0 || K == 0) return FG_OK;
     if (!dx || (N > 0 && (!dyq || !sdy || !wq || !sw))) return FG_ERR_INVALID_ARG;
     if (N % 128 != 0 || K % 128 != 0 || tiles(M, K) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(dyq) || !aligned16(wq) || !aligned16(dx) || !aligned4(sdy) || !aligned4(sw)) return FG_ERR_MISALIGNED;
-    return from_hip(fg_launch_gemm_dgrad(dyq, sdy, wq, sw, M, N, K, dx, out == FG_OUT_BF16, stream));
+    return from_hip(fg_launch_gemm_dgrad(dyq, sdy, wq, sw, M, N, K, dx, out == FG_OUT_BF16, scales == FG_SCALE_POW2, stream));
 }
 
 fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt, int64_t M,
-                            int64_t N, int64_t K, float* dw, int accumulate, hipStream_t stream) {
-    if (M < 0 || N < 0 || K < 0) return FG_ERR_INVALID_ARG;
+                            int64_t N, int64_t K, float* dw, int accumulate, fg_scale_mode scales, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
     if (N == 0 || K == 0) return FG_OK;
     if (!dw || (M > 0 && (!dytq || !sdyt || !xtq || !sxt))) return FG_ERR_INVALID_ARG;
     if (M % 128 != 0 || K % 4 != 0 || tiles(N, K) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(dytq) || !aligned16(xtq) || !aligned16(dw) || !aligned16(sxt) || !aligned4(sdyt))
         return FG_ERR_MISALIGNED;
-    return from_hip(fg_launch_gemm_wgrad(dytq, sdyt, xtq, sxt, M, N, K, dw, accumulate != 0, stream));
+    return from_hip(fg_launch_gemm_wgrad(dytq, sdyt, xtq, sxt, M, N, K, dw, accumulate != 0, scales == FG_SCALE_POW2, stream));
 }
 
 fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                               const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K, void* y,
-                              fg_out_dtype out, hipStream_t stream) {
-    if (G < 1 || G > kMaxGroups || total_rows < 0 || N < 0 || K < 0 || !valid_out(out)) return FG_ERR_INVALID_ARG;
+                              fg_out_dtype out, fg_scale_mode scales, hipStream_t stream) {
+    if (G < 1 || G > kMaxGroups || total_rows < 0 || N < 0 || K < 0 || !valid_out(out) || !valid_mode(scales))
+        return FG_ERR_INVALID_ARG;
     if (total_rows == 0 || N == 0) return FG_OK;
     if (!y || !d_offsets || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
     if (K % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-    if (((total_rows + 255) / 256 + G) * ((N + 255) / 256) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (((total_rows + 255) / 256 + G) * ((N + 127) / 128) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw) || !aligned4(d_offsets))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_grouped(xq, sx, wq, sw, d_offsets, G, total_rows, N, K, y, out == FG_OUT_BF16,
-                                           stream));
+                                           scales == FG_SCALE_POW2, stream));
 }
 
 }  // extern "C"

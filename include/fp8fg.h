@@ -41,6 +41,13 @@
  * The matrix core's summation inside a block is hardware-defined; results agree with the exact value to
  * within a max relative error of 1e-3 (FP32 output) / 1e-2 (BF16 output), normwise.
  *
+ * Every GEMM takes `scales`, the mode its operands were quantized in. FG_SCALE_FP32 accepts any fp32
+ * scales and promotes with a VALU FMA per element and block, as above. FG_SCALE_POW2 declares that every
+ * scale is an exact power of two in [2^-126, 2^127] (what the quantizers write in that mode): the matrix
+ * core then applies the scales itself (E8M0 block-scale operands of v_mfma_scale_f32_16x16x128_f8f6f4) and
+ * adds 2^(ea+eb) * P_b straight into the FP32 accumulator, which is the same promotion with an exact
+ * scale product and no VALU work. Passing FG_SCALE_POW2 with other scales gives unspecified results.
+ *
  * Layouts are row-major. "ld" arguments are row strides in elements.
  * Activation scales are MN-major: scale[group][row] (rows contiguous), so one 128-deep K step of a GEMM
  * reads its rows' scales as one contiguous run.
@@ -102,7 +109,7 @@ fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_
  *   K == 0 writes zeros). Pointers 16-byte aligned. */
 fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* y, fg_out_dtype out,
-                            hipStream_t stream);
+                            fg_scale_mode scales, hipStream_t stream);
 
 /* Dgrad (Figure 6, activation backward pass): dX[M][K] = dY[M][N] . W[N][K], contracting over N.
  *   dyq u8 [M][N], sdy f32 [N/128][M]   (dY quantized FG_ALONG_COLS)
@@ -112,7 +119,7 @@ fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* w
  *   dx  [M][K] f32 or bf16.  N % 128 == 0, K % 128 == 0, any M. */
 fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* dx, fg_out_dtype out,
-                            hipStream_t stream);
+                            fg_scale_mode scales, hipStream_t stream);
 
 /* Wgrad (Figure 6, weight backward pass): dW[N][K] (+)= dY[M][N]^T . X[M][K], contracting over the M
  * tokens, from token-dimension quantized operands:
@@ -123,7 +130,7 @@ fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t*
  *   M % 128 == 0; any N, K >= 0 with K % 4 == 0. */
 fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
                             int64_t M, int64_t N, int64_t K, float* dw, int accumulate,
-                            hipStream_t stream);
+                            fg_scale_mode scales, hipStream_t stream);
 
 /* Grouped Fprop for the routed experts of one GPU ([W4]: MoE layers of 256 routed experts with expert
  * intermediate dimension 2048, 8 active per token; [W5]: each GPU hosts 8 experts). For each group g:
@@ -133,7 +140,8 @@ fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_
  *   not re-checked on the host). K % 128 == 0, G >= 1. */
 fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                               const int32_t* d_offsets, int32_t G, int64_t total_rows,
-                              int64_t N, int64_t K, void* y, fg_out_dtype out, hipStream_t stream);
+                              int64_t N, int64_t K, void* y, fg_out_dtype out, fg_scale_mode scales,
+                              hipStream_t stream);
 
 /* Static description of a status code. */
 const char* fg_status_string(fg_status s);

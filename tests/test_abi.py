@@ -69,22 +69,23 @@ def test_quantize_w_rejections(L):
 
 def test_gemm_rejections(L):
     f = L.fg_fp8_gemm_fprop
-    assert f(A16, A16, A16, A16, 128, 128, 100, A16, 0, None) == SHAPE     # K % 128
-    assert f(A16, A16, A16, A16, 128, 128, 128, A16, 7, None) == INVALID   # bad out dtype
-    assert f(A16, A16, None, A16, 128, 128, 128, A16, 0, None) == INVALID  # null W
-    assert f(A16, A16, A16, A16, 128, 128, 128, ODD, 0, None) == MISALIGNED
-    assert f(None, None, None, None, 0, 128, 128, None, 0, None) == OK     # empty
+    assert f(A16, A16, A16, A16, 128, 128, 100, A16, 0, 0, None) == SHAPE     # K % 128
+    assert f(A16, A16, A16, A16, 128, 128, 128, A16, 7, 0, None) == INVALID   # bad out dtype
+    assert f(A16, A16, A16, A16, 128, 128, 128, A16, 0, 9, None) == INVALID   # bad scale mode
+    assert f(A16, A16, None, A16, 128, 128, 128, A16, 0, 0, None) == INVALID  # null W
+    assert f(A16, A16, A16, A16, 128, 128, 128, ODD, 0, 0, None) == MISALIGNED
+    assert f(None, None, None, None, 0, 128, 128, None, 0, 0, None) == OK     # empty
     d = L.fg_fp8_gemm_dgrad
-    assert d(A16, A16, A16, A16, 128, 200, 128, A16, 0, None) == SHAPE     # N (contraction) % 128
-    assert d(A16, A16, A16, A16, 128, 256, 200, A16, 0, None) == SHAPE     # K % 128
+    assert d(A16, A16, A16, A16, 128, 200, 128, A16, 0, 0, None) == SHAPE     # N (contraction) % 128
+    assert d(A16, A16, A16, A16, 128, 256, 200, A16, 0, 0, None) == SHAPE     # K % 128
     w = L.fg_fp8_gemm_wgrad
-    assert w(A16, A16, A16, A16, 100, 128, 128, A16, 0, None) == SHAPE     # M (tokens) % 128
-    assert w(A16, A16, A16, A16, 128, 128, 130, A16, 0, None) == SHAPE     # K % 4
-    assert w(A16, A16, A16, ODD, 128, 128, 128, A16, 0, None) == MISALIGNED  # per-row scales need 16 B
+    assert w(A16, A16, A16, A16, 100, 128, 128, A16, 0, 0, None) == SHAPE     # M (tokens) % 128
+    assert w(A16, A16, A16, A16, 128, 128, 130, A16, 0, 0, None) == SHAPE     # K % 4
+    assert w(A16, A16, A16, ODD, 128, 128, 128, A16, 0, 0, None) == MISALIGNED  # per-row scales need 16 B
     g = L.fg_fp8_grouped_gemm
-    assert g(A16, A16, A16, A16, A16B, 0, 128, 128, 128, A16, 0, None) == INVALID   # G < 1
-    assert g(A16, A16, A16, A16, None, 2, 128, 128, 128, A16, 0, None) == INVALID   # null offsets
-    assert g(A16, A16, A16, A16, A16B, 2, 128, 128, 100, A16, 0, None) == SHAPE     # K % 128
+    assert g(A16, A16, A16, A16, A16B, 0, 128, 128, 128, A16, 0, 0, None) == INVALID   # G < 1
+    assert g(A16, A16, A16, A16, None, 2, 128, 128, 128, A16, 0, 0, None) == INVALID   # null offsets
+    assert g(A16, A16, A16, A16, A16B, 2, 128, 128, 100, A16, 0, 0, None) == SHAPE     # K % 128
     assert L.fg_last_hip_error() == 0
 
 

@@ -46,7 +46,7 @@ def _rand_act(rng, rows, cols, std=1.0):
 def _fprop_case(x, w, bf16, pow2=False, pts=None):
     xq, sx = fg.fg_quantize_act_1x128(to_dev(x), pow2=pow2)
     wq, sw = fg.fg_quantize_w_128x128(to_dev(w), pow2=pow2)
-    y = fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16 if bf16 else torch.float32)
+    y = fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16 if bf16 else torch.float32, pow2=pow2)
     torch.cuda.synchronize()
     xq_n, sx_n, wq_n, sw_n = np_u8(xq), sx.cpu().numpy(), np_u8(wq), sw.cpu().numpy()
     # the codes the GEMM consumed are the oracle's codes (checked bit-exact in the quantizer tests);
@@ -138,13 +138,13 @@ def test_fprop_deterministic(dsv3):
 # Dgrad
 # ------------------------------------------------------------------------------------------------
 
-def _dgrad_case(dy, w, bf16, pts=None):
-    dyq, sdy = fg.fg_quantize_act_1x128(to_dev(dy))
-    wq, sw = fg.fg_quantize_w_128x128(to_dev(w))
-    dx = fg.fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.bfloat16 if bf16 else torch.float32)
+def _dgrad_case(dy, w, bf16, pts=None, pow2=False):
+    dyq, sdy = fg.fg_quantize_act_1x128(to_dev(dy), pow2=pow2)
+    wq, sw = fg.fg_quantize_w_128x128(to_dev(w), pow2=pow2)
+    dx = fg.fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.bfloat16 if bf16 else torch.float32, pow2=pow2)
     torch.cuda.synchronize()
-    dyq_o, sdy_o = oracle.quantize_act_1x128(bits(dy), 0, False)
-    wq_o, sw_o = oracle.quantize_w_128x128(bits(w), False)
+    dyq_o, sdy_o = oracle.quantize_act_1x128(bits(dy), 0, pow2)
+    wq_o, sw_o = oracle.quantize_w_128x128(bits(w), pow2)
     assert np.array_equal(np_u8(dyq), dyq_o) and np.array_equal(np_u8(wq), wq_o)
     prom, exact = oracle.gemm_dgrad(dyq_o, sdy_o, wq_o, sw_o, out_bf16=bf16, pts=pts)
     yo = _out_np(dx, bf16).reshape(-1)
@@ -154,18 +154,20 @@ def _dgrad_case(dy, w, bf16, pts=None):
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (37, 256, 128), (300, 384, 640), (256, 128, 256), (100, 512, 384)])
 @pytest.mark.parametrize("bf16", [False, True])
-def test_dgrad_shapes(M, N, K, bf16):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_dgrad_shapes(M, N, K, bf16, pow2):
     device()
     rng = np.random.default_rng(M * 13 + N * 5 + K)
-    _dgrad_case(_rand_act(rng, M, N, 1e-3), wl.normal_bf16(rng, (N, K), 0.02), bf16)
+    _dgrad_case(_rand_act(rng, M, N, 1e-3), wl.normal_bf16(rng, (N, K), 0.02), bf16, pow2=pow2)
 
 
-def test_dgrad_dsv3_full_size_sampled(dsv3):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_dgrad_dsv3_full_size_sampled(dsv3, pow2):
     x, w, dy = dsv3
     M, N = dy.shape
     K = w.shape[1]
     pts = sample_points(M, K, 2000, seed=12)
-    err, y, exact = _dgrad_case(dy, w, bf16=False, pts=pts)
+    err, y, exact = _dgrad_case(dy, w, bf16=False, pts=pts, pow2=pow2)
     assert normwise(y, exact) <= TOL_F32
 
 
@@ -173,18 +175,18 @@ def test_dgrad_dsv3_full_size_sampled(dsv3):
 # Wgrad
 # ------------------------------------------------------------------------------------------------
 
-def _wgrad_case(dy, x, pts=None, init=None):
-    dytq, sdyt = fg.fg_quantize_act_1x128(to_dev(dy), axis=fg.FG_ALONG_ROWS)
-    xtq, sxt = fg.fg_quantize_act_1x128(to_dev(x), axis=fg.FG_ALONG_ROWS)
+def _wgrad_case(dy, x, pts=None, init=None, pow2=False):
+    dytq, sdyt = fg.fg_quantize_act_1x128(to_dev(dy), axis=fg.FG_ALONG_ROWS, pow2=pow2)
+    xtq, sxt = fg.fg_quantize_act_1x128(to_dev(x), axis=fg.FG_ALONG_ROWS, pow2=pow2)
     N, K = dy.shape[1], x.shape[1]
     if init is not None:
         dw = to_dev(torch.from_numpy(init))
-        dw = fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw, accumulate=True)
+        dw = fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw, accumulate=True, pow2=pow2)
     else:
-        dw = fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt)
+        dw = fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, pow2=pow2)
     torch.cuda.synchronize()
-    dytq_o, sdyt_o = oracle.quantize_act_1x128(bits(dy), 1, False)
-    xtq_o, sxt_o = oracle.quantize_act_1x128(bits(x), 1, False)
+    dytq_o, sdyt_o = oracle.quantize_act_1x128(bits(dy), 1, pow2)
+    xtq_o, sxt_o = oracle.quantize_act_1x128(bits(x), 1, pow2)
     assert np.array_equal(np_u8(dytq), dytq_o) and np.array_equal(np_u8(xtq), xtq_o)
     init_sel = None if init is None else (init.reshape(-1) if pts is None else init.reshape(-1)[pts])
     prom, exact = oracle.gemm_wgrad(dytq_o, sdyt_o, xtq_o, sxt_o, dw_init=init_sel, pts=pts)
@@ -194,25 +196,28 @@ def _wgrad_case(dy, x, pts=None, init=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 8, 8), (128, 40, 264), (256, 296, 384), (384, 256, 128), (512, 136, 72)])
-def test_wgrad_shapes(M, N, K):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_wgrad_shapes(M, N, K, pow2):
     device()
     rng = np.random.default_rng(M + N * 3 + K * 11)
-    _wgrad_case(_rand_act(rng, M, N, 1e-3), _rand_act(rng, M, K))
+    _wgrad_case(_rand_act(rng, M, N, 1e-3), _rand_act(rng, M, K), pow2=pow2)
 
 
-def test_wgrad_accumulate():
+@pytest.mark.parametrize("pow2", [False, True])
+def test_wgrad_accumulate(pow2):
     device()
     rng = np.random.default_rng(5)
     M, N, K = 256, 200, 136
     init = rng.standard_normal((N, K)).astype(np.float32) * 1e-3
-    _wgrad_case(_rand_act(rng, M, N, 1e-3), _rand_act(rng, M, K), init=init)
+    _wgrad_case(_rand_act(rng, M, N, 1e-3), _rand_act(rng, M, K), init=init, pow2=pow2)
 
 
-def test_wgrad_dsv3_full_size_sampled(dsv3):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_wgrad_dsv3_full_size_sampled(dsv3, pow2):
     x, w, dy = dsv3
     N, K = dy.shape[1], x.shape[1]
     pts = sample_points(N, K, 2000, seed=13)
-    err, y, exact = _wgrad_case(dy, x, pts=pts)
+    err, y, exact = _wgrad_case(dy, x, pts=pts, pow2=pow2)
     assert normwise(y, exact) <= TOL_F32
 
 
@@ -220,20 +225,20 @@ def test_wgrad_dsv3_full_size_sampled(dsv3):
 # Grouped (MoE experts)
 # ------------------------------------------------------------------------------------------------
 
-def _grouped_case(x, w, offsets, bf16=True, pts=None):
-    xq, sx = fg.fg_quantize_act_1x128(to_dev(x))
+def _grouped_case(x, w, offsets, bf16=True, pts=None, pow2=False):
+    xq, sx = fg.fg_quantize_act_1x128(to_dev(x), pow2=pow2)
     G, N, K = w.shape
     wq = torch.empty((G, N, K), dtype=torch.uint8, device=device())
     sw = torch.empty((G, (N + 127) // 128, K // 128), dtype=torch.float32, device=device())
     wd = to_dev(w)
     for g in range(G):
-        fg.fg_quantize_w_128x128(wd[g], q=wq[g], scales=sw[g])
+        fg.fg_quantize_w_128x128(wd[g], q=wq[g], scales=sw[g], pow2=pow2)
     off = torch.from_numpy(np.asarray(offsets, np.int32)).to(device())
-    y = fg.fg_fp8_grouped_gemm(xq, sx, wq, sw, off, out_dtype=torch.bfloat16 if bf16 else torch.float32)
+    y = fg.fg_fp8_grouped_gemm(xq, sx, wq, sw, off, out_dtype=torch.bfloat16 if bf16 else torch.float32, pow2=pow2)
     torch.cuda.synchronize()
-    xq_o, sx_o = oracle.quantize_act_1x128(bits(x), 0, False)
+    xq_o, sx_o = oracle.quantize_act_1x128(bits(x), 0, pow2)
     assert np.array_equal(np_u8(xq), xq_o)
-    wo = [oracle.quantize_w_128x128(bits(w[g]), False) for g in range(G)]
+    wo = [oracle.quantize_w_128x128(bits(w[g]), pow2) for g in range(G)]
     wq_o, sw_o = np.stack([a for a, _ in wo]), np.stack([b for _, b in wo])
     assert np.array_equal(np_u8(wq), wq_o)
     prom, exact = oracle.gemm_grouped(xq_o, sx_o, wq_o, sw_o, offsets, out_bf16=bf16, pts=pts)
@@ -243,14 +248,15 @@ def _grouped_case(x, w, offsets, bf16=True, pts=None):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-def test_grouped_small_with_empty_groups(bf16):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_small_with_empty_groups(bf16, pow2):
     device()
     rng = np.random.default_rng(21)
     offsets = [0, 0, 300, 301, 301, 700, 957]            # empty groups at 0 and 3, a 1-row group
     T, K, N = offsets[-1], 256, 136
     x = _rand_act(rng, T, K)
     w = wl.normal_bf16(rng, (len(offsets) - 1, N, K), 0.02)
-    _grouped_case(x, w, offsets, bf16)
+    _grouped_case(x, w, offsets, bf16, pow2=pow2)
 
 
 def test_grouped_moe_share_full_size_sampled():
