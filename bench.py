@@ -11,7 +11,10 @@ stream the kernels run on. Also reported: per-kernel roofline fractions, cold-ca
 (a 1 GiB scrub between launches defeats the 256 MB Infinity Cache), the grouped MoE GEMM on one GPU's
 expert share, and the CPU oracle timed on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-moe] [--no-cpu] [--calib-copy]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pow2] [--no-moe] [--no-cpu] [--no-cold] [--calib-copy]
+
+The headline uses fp32 scales (amax/448); --pow2 makes power-of-2 scales the headline. The other mode is
+always measured too, on the same inputs, and reported under "other_scale_mode".
 """
 import argparse
 import hashlib
@@ -105,53 +108,64 @@ def main():
         dw=torch.empty((N, K), dtype=f32, device=dev),
     )
     B = bufs
+
+    def make_ops(pow2):
+        return [
+            ("quant_x_rowwise", lambda: fg.fg_quantize_act_1x128(x, q=B["xq"], scales=B["sx"], pow2=pow2),
+             "hbm", quant_bytes(M, K)),
+            ("quant_w_128x128", lambda: fg.fg_quantize_w_128x128(w, q=B["wq"], scales=B["sw"], pow2=pow2),
+             "hbm", quant_w_bytes(N, K)),
+            ("fprop", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=pow2),
+             "mfma", 2.0 * M * N * K),
+            ("quant_dy_rowwise", lambda: fg.fg_quantize_act_1x128(dy, q=B["dyq"], scales=B["sdy"], pow2=pow2),
+             "hbm", quant_bytes(M, N)),
+            ("dgrad", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"], pow2=pow2),
+             "mfma", 2.0 * M * N * K),
+            ("quant_dy_tokendim", lambda: fg.fg_quantize_act_1x128(dy, axis=fg.FG_ALONG_ROWS, q=B["dytq"],
+                                                                   scales=B["sdyt"], pow2=pow2),
+             "hbm", quant_bytes(M, N)),
+            ("quant_x_tokendim", lambda: fg.fg_quantize_act_1x128(x, axis=fg.FG_ALONG_ROWS, q=B["xtq"],
+                                                                  scales=B["sxt"], pow2=pow2),
+             "hbm", quant_bytes(M, K)),
+            ("wgrad", lambda: fg.fg_fp8_gemm_wgrad(B["dytq"], B["sdyt"], B["xtq"], B["sxt"], dw=B["dw"], pow2=pow2),
+             "mfma", 2.0 * M * N * K),
+        ]
+
+    def measure(ops, steps, warmup, tag):
+        """W untimed steps, then exactly `steps` timed steps between two device synchronisations; HIP events
+        recorded on the kernels' own stream around every launch give the per-kernel times."""
+        def run_step(events=None):
+            for i, (_, fn, _, _) in enumerate(ops):
+                if events is not None:
+                    events[i][0].record(stream)
+                fn()
+                if events is not None:
+                    events[i][1].record(stream)
+
+        for _ in range(warmup):
+            run_step()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            run_step(ev[s])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / steps
+        per = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+               for i, (name, _, _, _) in enumerate(ops)}
+        print(f"[bench] {tag}: timed {steps} steps after {warmup} warmup: {ms:.3f} ms/step", file=sys.stderr,
+              flush=True)
+        return ms, per
+
     POW2 = bool(args.pow2)
-    ops = [
-        ("quant_x_rowwise", lambda: fg.fg_quantize_act_1x128(x, q=B["xq"], scales=B["sx"], pow2=POW2),
-         "hbm", quant_bytes(M, K)),
-        ("quant_w_128x128", lambda: fg.fg_quantize_w_128x128(w, q=B["wq"], scales=B["sw"], pow2=POW2),
-         "hbm", quant_w_bytes(N, K)),
-        ("fprop", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=POW2),
-         "mfma", 2.0 * M * N * K),
-        ("quant_dy_rowwise", lambda: fg.fg_quantize_act_1x128(dy, q=B["dyq"], scales=B["sdy"], pow2=POW2),
-         "hbm", quant_bytes(M, N)),
-        ("dgrad", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"], pow2=POW2),
-         "mfma", 2.0 * M * N * K),
-        ("quant_dy_tokendim", lambda: fg.fg_quantize_act_1x128(dy, axis=fg.FG_ALONG_ROWS, q=B["dytq"], scales=B["sdyt"],
-                                                               pow2=POW2),
-         "hbm", quant_bytes(M, N)),
-        ("quant_x_tokendim", lambda: fg.fg_quantize_act_1x128(x, axis=fg.FG_ALONG_ROWS, q=B["xtq"], scales=B["sxt"],
-                                                              pow2=POW2),
-         "hbm", quant_bytes(M, K)),
-        ("wgrad", lambda: fg.fg_fp8_gemm_wgrad(B["dytq"], B["sdyt"], B["xtq"], B["sxt"], dw=B["dw"], pow2=POW2),
-         "mfma", 2.0 * M * N * K),
-    ]
-
-    def run_step(events=None):
-        for i, (_, fn, _, _) in enumerate(ops):
-            if events is not None:
-                events[i][0].record(stream)
-            fn()
-            if events is not None:
-                events[i][1].record(stream)
-
-    for _ in range(args.warmup):
-        run_step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(ev[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    per_kernel_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
-                     for i, (name, _, _, _) in enumerate(ops)}
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    ops = make_ops(POW2)
+    ms_per_step, per_kernel_ms = measure(ops, args.steps, args.warmup, "pow2 scales" if POW2 else "fp32 scales")
+    # The other scale mode, same buffers and shapes, reported beside the headline.
+    alt_ops = make_ops(not POW2)
+    alt_ms, alt_per = measure(alt_ops, args.steps, args.warmup, "fp32 scales" if POW2 else "pow2 scales")
 
     gemm_flop = 3 * 2.0 * M * N * K
     value = gemm_flop / (ms_per_step * 1e-3) / 1e12
@@ -268,6 +282,12 @@ def main():
         "cpu_baseline": cpu,
         "quantize_GBps_in_step": round(qbytes / (qms * 1e-3) / 1e9, 1),
         "kernels": kernels,
+        "other_scale_mode": {
+            "scale_mode": "fp32" if POW2 else "pow2", "ms_per_step": round(alt_ms, 4),
+            "value": round(gemm_flop / (alt_ms * 1e-3) / 1e12, 2),
+            "gemm_TFLOP/s": {n: round(2.0 * M * N * K / (alt_per[n] * 1e-3) / 1e12, 1)
+                             for n, _, b, _ in alt_ops if b == "mfma"},
+            "kernel_ms": {n: round(v, 4) for n, v in alt_per.items()}},
         "quantize_cold_cache": cold,
         "moe_grouped": moe,
         "kernel_source_hash": kernel_source_hash(),
