@@ -1,0 +1,86 @@
+"""GPU accuracy on the accumulation-stress workload: X [1024, K], W [1024, K] ~ U(0, 1), K in {4096, 16384}.
+
+All products are positive, so every output is a long sum of same-signed terms: the case where a
+limited-precision accumulator loses most. The pages (fine-grained quantization / increasing accumulation
+precision sections) report an error of nearly 2% at K = 4096 for an accumulator kept inside the matrix
+core, and remove it by promoting partial sums into FP32 every 128 elements of K.
+
+Checked here against the oracle's exact (fp64) value of the same quantized operands, elementwise:
+  * fp32 scales: the product path, per-128 promotion by a VALU FMA;
+  * pow2 scales: the matrix core accumulates every 128-K block straight into its FP32 accumulator (the
+    gfx950 scaled MFMA chain), no VALU promotion at all;
+  * the oracle's emulation of the limited accumulator (p explicit mantissa bits, no promotion) on the
+    same outputs, which must be orders of magnitude worse at K = 4096 and grow with K.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_fine_grained_amax_amd as fg
+import oracle
+from fp8_fine_grained_amax_amd import workloads as wl
+from tests.gpu_util import TOL_F32, bits, device, normwise, np_u8, sample_points, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(K, pow2):
+    x, w = wl.accumulation_stress(K)
+    xq, sx = fg.fg_quantize_act_1x128(to_dev(x), pow2=pow2)
+    wq, sw = fg.fg_quantize_w_128x128(to_dev(w), pow2=pow2)
+    y = fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.float32, pow2=pow2)
+    torch.cuda.synchronize()
+    xq_o, sx_o = oracle.quantize_act_1x128(bits(x), 0, pow2)
+    wq_o, sw_o = oracle.quantize_w_128x128(bits(w), pow2)
+    assert np.array_equal(np_u8(xq), xq_o) and np.array_equal(sx.cpu().numpy(), sx_o)
+    assert np.array_equal(np_u8(wq), wq_o) and np.array_equal(sw.cpu().numpy(), sw_o)
+    return y.cpu().numpy(), (xq_o, sx_o, wq_o, sw_o)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_accumulation_stress_k4096_full(pow2):
+    device()
+    y, ops = _case(4096, pow2)
+    prom, exact = oracle.gemm_fprop(*ops)
+    assert normwise(y, prom) <= TOL_F32
+    rel = np.max(np.abs(y.astype(np.float64) - exact) / np.abs(exact))
+    print(f"\n[accum] K=4096 {'pow2 (MFMA chain)' if pow2 else 'fp32 (VALU promotion)'}: "
+          f"elementwise max rel err vs exact = {rel:.3e}")
+    assert rel <= TOL_F32
+    # every output is a sum of 4096 positive products: FP32 promotion keeps it within a few ulps
+    assert rel <= 1e-5
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_accumulation_stress_k16384_sampled(pow2):
+    device()
+    y, ops = _case(16384, pow2)
+    pts = sample_points(1024, 1024, 4000, seed=41)
+    prom, exact = oracle.gemm_fprop(*ops, pts=pts)
+    yo = y.reshape(-1)[pts]
+    assert normwise(yo, prom) <= TOL_F32
+    rel = np.max(np.abs(yo.astype(np.float64) - exact) / np.abs(exact))
+    print(f"\n[accum] K=16384 {'pow2 (MFMA chain)' if pow2 else 'fp32 (VALU promotion)'}: "
+          f"elementwise max rel err vs exact = {rel:.3e}")
+    assert rel <= 1e-5
+
+
+def test_promotion_beats_limited_accumulator():
+    """The GPU's promoted result against the oracle's limited-accumulator emulation on the same outputs."""
+    device()
+    errs = {}
+    for K in (4096, 16384):
+        y, ops = _case(K, False)
+        pts = sample_points(1024, 1024, 1000, seed=43)
+        _, exact = oracle.gemm_fprop(*ops, pts=pts)
+        gpu = np.max(np.abs(y.reshape(-1)[pts].astype(np.float64) - exact) / np.abs(exact))
+        row = {"gpu_promoted": gpu}
+        for p in (10, 11, 12, 13, 14):
+            lim = oracle.gemm_fprop_limited(*ops, chunk=32, bits=p, pts=pts)
+            row[f"limited_p{p}"] = np.max(np.abs(lim - exact) / np.abs(exact))
+        errs[K] = row
+        print(f"\n[accum] K={K}: " + ", ".join(f"{k} {v:.3e}" for k, v in row.items()))
+    assert errs[4096]["limited_p10"] > 1e-2                     # the pages' percent-level error
+    assert errs[16384]["limited_p10"] > errs[4096]["limited_p10"]  # grows with K
+    for K in (4096, 16384):
+        assert errs[K]["gpu_promoted"] * 100 < errs[K]["limited_p14"]
