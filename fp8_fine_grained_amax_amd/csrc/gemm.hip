@@ -9,40 +9,63 @@
 // "5 Ways You can get More Deepseek While Spending Less"), with the dequantization folded into the same
 // step (per-group scaling along the inner dimension, same page). On the pages' H800 the promotion ran on
 // CUDA cores while a second warpgroup kept the tensor cores busy (untitled gnrental.net page); here the
-// MFMA of one 16x16 tile runs while the VALU promotes the previous one, inside each wave.
+// MFMAs of one row of 16x16 tiles run while the VALU promotes the previous row, inside each wave.
+// With power-of-two scales the MFMA's own E8M0 scale operands apply them and the partial goes straight
+// into the FP32 accumulator.
 //
-// Workgroup tile 256 (M) x 192 (N) x 128 (K), 12 waves of 64 x 64 (3 waves per SIMD): 16 MFMAs and 64 FP32
-// accumulator VGPRs per wave per K step, so each wave stays under the 168-VGPR budget of 3 waves per SIMD
-// and the SIMD hides MFMA and LDS latency by switching between waves. Operand tiles go HBM -> LDS with
-// global_load_lds_dwordx4 (no register staging), double-buffered (2 x 58 KB). LDS rows are 16 B-chunk
-// swizzled so the fragment reads are bank-conflict-free. The MFMA is issued with the B-role fragment
-// first, so each lane ends up with one output row m and four consecutive output columns n (8 B bf16 /
-// 16 B fp32 stores). The DeepSeek-V3 dense-MLP Fprop (4096 x 18432) is exactly 1536 tiles: 6 full rounds
-// of 256 CUs.
+// Two workgroup shapes, chosen per launch (the one whose tiles fill the 256 CUs in the fewest rounds of
+// equal work):
+//   256 x 192 x 128, 12 waves (4 x 3) of 64 x 64: 3 waves per SIMD, 64 accumulator VGPRs per wave;
+//   256 x 256 x 128,  8 waves (2 x 4) of 128 x 64: 2 waves per SIMD, 128 accumulator VGPRs per wave; a
+//                     wave reads 25% fewer LDS bytes per MFMA, which also lowers the LDS power that
+//                     competes with the matrix cores for the chip's clock.
+// Operand tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging), double-buffered. The
+// next K step's loads are issued in pieces spread over the current step's MFMA rows. LDS rows are 16 B-chunk
+// swizzled so fragment reads are bank-conflict-free. The MFMA is issued with the B-role fragment first, so
+// each lane ends up with one output row m and four consecutive output columns n (8 B bf16 / 16 B fp32
+// stores).
 //
 // Variants:
 //   B_TRANS   B is stored [K][N] (the weight W[N_contr][K_out] read by Dgrad): the tile lands in LDS as
-//             [128 contraction rows][192 B] and fragments are read with ds_read_b64_tr_b8, the transposed
-//             LDS read (the capability the gnrental.net page asks future hardware for).
+//             [128 contraction rows][BN bytes] and fragments are read with ds_read_b64_tr_b8, the
+//             transposed LDS read (the capability the gnrental.net page asks future hardware for).
 //   SB_BLOCK  sB = sw[n/128][b]           (Fprop / grouped: 128x128 weight blocks)
 //   SB_BLOCK_T sB = sw[b][n/128]          (Dgrad: the same blocks, read along the other axis)
 //   SB_ROW    sB = sb[b][n]               (Wgrad: 1x128 tiles along tokens on both operands)
 //   GROUPED   rows split into per-group segments given by device offsets, B and sB per group.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 
 namespace {
 
-// Workgroup tile 256 (M) x 192 (N) x 128 (K), 12 waves in a 4 x 3 grid, wave tile 64 x 64.
-constexpr int BM = 256, BN = 192, BK = 128;
-constexpr int NWAVES = 12;
-constexpr int NTHREADS = NWAVES * 64;
-constexpr int WAVE_M = 64, WAVE_N = 64;
-constexpr int WAVES_N = BN / WAVE_N;                    // 3
-constexpr int MSUB = WAVE_M / 16, NSUB = WAVE_N / 16;   // 4 x 4 MFMA tiles per wave
-constexpr int STAGE_A = BM * BK;                        // 32 KB
-constexpr int STAGE_B = BN * BK;                        // 24 KB (NT: [192][128 B]; transposed: [128][192 B])
-constexpr int STAGE = STAGE_A + STAGE_B + 2048;         // + A and B scale slices (1 KB each)
-constexpr int LDS_BYTES = 2 * STAGE;                    // 116 KB, double-buffered
+constexpr int BK = 128;
+
+template <int WAVES_M_, int WAVES_N_, int WAVE_M_, int WAVE_N_>
+struct TileCfg {
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVE_M = WAVE_M_, WAVE_N = WAVE_N_;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int NTHREADS = NW * 64;
+    static constexpr int BM = WAVES_M * WAVE_M, BN = WAVES_N * WAVE_N;
+    static constexpr int MSUB = WAVE_M / 16, NSUB = WAVE_N / 16;
+    static constexpr int STAGE_A = BM * BK;
+    static constexpr int STAGE_B = BN * BK;             // NT: [BN][128 B]; transposed: [128][BN B]
+    static constexpr int SCALES_A = BM * 4, SCALES_B = BN * 4;
+    static constexpr int STAGE = STAGE_A + STAGE_B + SCALES_A + SCALES_B;
+    static constexpr int LDS_BYTES = 2 * STAGE;
+    // global_load_lds_dwordx4 instructions per stage (1 KB each) and per wave
+    static constexpr int LA = STAGE_A / 1024, LB = STAGE_B / 1024;
+    static constexpr int UA = (LA + NW - 1) / NW, UB = (LB + NW - 1) / NW;
+    static constexpr int SLICES_A = BM / 64, SLICES_B = BN / 64;   // 64-float scale slices
+    static constexpr int LOADS_PER_WAVE = UA + UB + 1;
+    static_assert(SLICES_A + SLICES_B <= NW, "one scale slice per wave");
+    static_assert(BN % 16 == 0 && BN <= 256, "transposed B rows hold at most 16 chunks");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+using Cfg12 = TileCfg<4, 3, 64, 64>;   // 256 x 192
+using Cfg8 = TileCfg<2, 4, 128, 64>;   // 256 x 256
 
 enum { SB_BLOCK = 0, SB_BLOCK_T = 1, SB_ROW = 2 };
 
@@ -67,11 +90,15 @@ struct GemmParams {
 // is stored at c ^ swz128(r): rows r..r+15 read at one logical chunk land on 16 distinct (row parity,
 // chunk) bank groups.
 __device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-// Transposed B tile [128 contraction rows][192 B]: chunk c of row r is stored at c ^ swzT(r) (only the
-// low two bits move, so chunks stay inside their aligned group of four, i.e. inside the 12-chunk row).
-// ds_read_b64_tr_b8 serves 32 lanes at a time: rows r..r+7 and r+32..r+39, two 8 B halves of one logical
-// chunk each; with the 192 B row stride these hit 32 distinct 8 B slots of the 256 B bank window.
-__device__ __forceinline__ int swzT(int r) { return ((r >> 2) & 1) | (((r >> 5) & 1) << 1); }
+// Transposed B tile [128 contraction rows][BN B]. ds_read_b64_tr_b8 serves 32 lanes at a time: rows
+// r..r+7 and r+32..r+39 (r a multiple of 8), 16 B of one logical chunk each. With a 192 B row stride the
+// rows already spread over the bank window and moving the two low chunk bits suffices; with a 256 B stride
+// every row starts at bank 0, so the chunk is XORed with all 16 distinct values (r & 7) | ((r >> 5 & 1) << 3).
+template <int BN>
+__device__ __forceinline__ int swzT(int r) {
+    if constexpr (BN == 256) return (r & 7) | (((r >> 5) & 1) << 3);
+    return ((r >> 2) & 1) | (((r >> 5) & 1) << 1);
+}
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
@@ -89,13 +116,15 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* tile16, int lo_off, int hi
 // E8M0 code of an fp32 power of two in [2^-127, 2^127]: its biased exponent field.
 __device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23) & 0xFF; }
 
-template <bool B_TRANS, int SBK, bool GROUPED, bool POW2>
-__global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
+template <class C, bool B_TRANS, int SBK, bool GROUPED, bool POW2>
+__global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
+    constexpr int BM = C::BM, BN = C::BN, NW = C::NW, MSUB = C::MSUB, NSUB = C::NSUB;
+    constexpr int WAVE_M = C::WAVE_M, WAVE_N = C::WAVE_N;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t N = p.N, K = p.K;
     const int64_t lda = K;
     const bool vec_ok = (N & 3) == 0;       // output rows are 16 B (fp32) / 8 B (bf16) aligned
@@ -144,40 +173,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         n0 = (int64_t)nt * BN;
     }
 
-    // LDS stage st: [A 32 KB][B 24 KB][A scales 1 KB][B scales 1 KB (per-row B scales only)]
-    auto stA = [&](int st) { return smem + st * STAGE; };
-    auto stB = [&](int st) { return smem + st * STAGE + STAGE_A; };
-    auto stSA = [&](int st) { return reinterpret_cast<float*>(smem + st * STAGE + STAGE_A + STAGE_B); };
-    auto stSB = [&](int st) { return reinterpret_cast<float*>(smem + st * STAGE + STAGE_A + STAGE_B + 1024); };
+    // LDS stage st: [A][B][A scales (BM floats)][B scales (BN floats, per-row B scales only)]
+    auto stA = [&](int st) { return smem + st * C::STAGE; };
+    auto stB = [&](int st) { return smem + st * C::STAGE + C::STAGE_A; };
+    auto stSA = [&](int st) { return reinterpret_cast<float*>(smem + st * C::STAGE + C::STAGE_A + C::STAGE_B); };
+    auto stSB = [&](int st) {
+        return reinterpret_cast<float*>(smem + st * C::STAGE + C::STAGE_A + C::STAGE_B + C::SCALES_A);
+    };
 
     // ---------------- global -> LDS load plan (per thread, fixed over K) ----------------
     // Each global_load_lds_dwordx4 instruction fills 1 KB of LDS: lane l lands at byte 16 l of it.
-    // A: 32 instructions of 8 rows (instruction t: rows 8t .. 8t+7); wave w issues t = w, w+12, w+24.
+    // A: LA instructions of 8 rows (instruction t: rows 8t .. 8t+7); wave w issues t = w + NW u. A wave
+    // with fewer instructions than UA re-issues its previous one (same source, same LDS bytes: harmless),
+    // which keeps every wave's issue sequence identical and branch-free.
     // Lane l lands at row 8t + l/8, physical chunk l%8, and fetches logical chunk (l%8) ^ swz128(row).
     // Offsets are relative to wave-uniform tile bases (SGPRs) and fit in 32 bits.
     const uint8_t* a_tile = p.a + m0 * lda;
-    uint32_t a_off[3];
+    uint32_t a_off[C::UA];
+    int a_t[C::UA];
 #pragma unroll
-    for (int u = 0; u < 3; u++) {
-        const int t = wave + NWAVES * u;
-        const int row = (t * 8 + (lane >> 3)) & (BM - 1);
+    for (int u = 0; u < C::UA; u++) {
+        int t = wave + NW * u;
+        t = t < C::LA ? t : t - NW;
+        a_t[u] = t;
+        const int row = t * 8 + (lane >> 3);
         const int lch = (lane & 7) ^ swz128(row);
         int64_t gr = m0 + row;
         gr = gr < m_end ? gr : m_end - 1;
         a_off[u] = (uint32_t)((gr - m0) * lda + lch * 16);
     }
-    const int a_count = wave + NWAVES * 2 < BM / 8 ? 3 : 2;
-    // B (NT): 24 instructions of 8 rows, wave w issues t = w, w+12.
-    // B (transposed): [128][192 B] = 24 instructions of 1 KB; flat 16 B slot f = 64 t + l is row f/12,
-    // physical chunk f%12, holding logical chunk (f%12) ^ swzT(row) (output columns 16 * logical ..).
+    // B (NT): LB instructions of 8 rows. B (transposed): [128][BN B], LB instructions of 1 KB; flat 16 B
+    // slot f = 64 t + l is row f / (BN/16), physical chunk f % (BN/16), holding logical chunk
+    // pch ^ swzT(row) (output columns 16 * logical ..).
     const uint8_t* b_tile;
-    uint32_t b_off[2];
+    uint32_t b_off[C::UB];
+    int b_t[C::UB];
+#pragma unroll
+    for (int u = 0; u < C::UB; u++) {
+        int t = wave + NW * u;
+        t = t < C::LB ? t : t - NW;
+        b_t[u] = t;
+    }
     if constexpr (!B_TRANS) {
         b_tile = Bp + n0 * K;
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int t = wave + NWAVES * u;
-            const int row = t * 8 + (lane >> 3);
+        for (int u = 0; u < C::UB; u++) {
+            const int row = b_t[u] * 8 + (lane >> 3);
             const int lch = (lane & 7) ^ swz128(row);
             int64_t gr = n0 + row;
             gr = gr < N ? gr : N - 1;
@@ -185,67 +226,53 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         }
     } else {
         b_tile = Bp;
+        constexpr int CPR = BN / 16;          // 16 B chunks per transposed row
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int f = (wave + NWAVES * u) * 64 + lane;
-            const int row = f / 12, pch = f % 12;
-            const int lch = pch ^ swzT(row);
+        for (int u = 0; u < C::UB; u++) {
+            const int f = b_t[u] * 64 + lane;
+            const int row = f / CPR, pch = f % CPR;
+            const int lch = pch ^ swzT<BN>(row);
             int64_t gc = n0 + lch * 16;
             gc = gc < N ? gc : N - 16;
             b_off[u] = (uint32_t)((int64_t)row * N + gc);
         }
     }
-    // Scales of one K step: the tile's 256 A rows (waves 0-3, one float per lane) and, for per-row B
-    // scales, the tile's 192 B rows (waves 4-6); rows past the end re-read the last valid row.
-    int64_t sc_row = 0;
-    if (wave < 4) {
-        sc_row = m0 + wave * 64 + lane;
-        sc_row = sc_row < p.sa_ld ? sc_row : p.sa_ld - 1;
-    } else if (wave < 7) {
-        sc_row = n0 + (wave - 4) * 64 + lane;
+    // Scales of one K step: slice s (64 floats) of the tile's BM A rows (s < SLICES_A) or, for per-row B
+    // scales, of its BN B rows. Wave w loads slice w; waves past the last slice re-load an A slice. Rows
+    // past the end re-read the last valid row.
+    const int n_slices = SBK == SB_ROW ? C::SLICES_A + C::SLICES_B : C::SLICES_A;
+    const int sc_slice = wave < n_slices ? wave : wave % C::SLICES_A;
+    const bool sc_is_b = SBK == SB_ROW && sc_slice >= C::SLICES_A;
+    int64_t sc_row;
+    if (sc_is_b) {
+        sc_row = n0 + (sc_slice - C::SLICES_A) * 64 + lane;
         sc_row = sc_row < N ? sc_row : N - 1;
+    } else {
+        sc_row = m0 + sc_slice * 64 + lane;
+        sc_row = sc_row < p.sa_ld ? sc_row : p.sa_ld - 1;
     }
+    const int sc_dst = sc_is_b ? C::SCALES_A + (sc_slice - C::SLICES_A) * 256 : sc_slice * 256;
 
-    // Staging loads of one K step: every wave issues exactly six (3 A + 2 B + 1 scale slice), branch-free,
-    // in four pieces spread over the step's four M-tile MFMA groups: a burst of all of them right after
-    // the barrier stalls the issuing waves in the memory pipeline before their MFMAs. Waves 8-11 own only
-    // two A instructions and waves 7-11 no scale slice: they re-issue one of their own loads (same source,
-    // same LDS bytes), which is harmless.
-    const int a_u2 = a_count == 3 ? 2 : 0;
-    const int sc_wave = wave < 7 ? wave : (wave - 7) & 3;
-    if (wave >= 7) {
-        int64_t r = m0 + sc_wave * 64 + lane;
-        sc_row = r < p.sa_ld ? r : p.sa_ld - 1;
-    }
-    auto issue_piece = [&](int kb, int st, int piece) {
-        const uint8_t* a_k = a_tile + (int64_t)kb * BK;
-        const uint8_t* b_k = B_TRANS ? b_tile + (int64_t)kb * BK * N : b_tile + (int64_t)kb * BK;
-        if (piece == 0) {
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(a_k + a_off[0]), FG_LDS(stA(st) + wave * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(a_k + a_off[1]), FG_LDS(stA(st) + (wave + NWAVES) * 1024), 16, 0,
-                                             0);
-        } else if (piece == 1) {
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(a_k + a_off[a_u2]), FG_LDS(stA(st) + (wave + NWAVES * a_u2) * 1024),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(b_k + b_off[0]), FG_LDS(stB(st) + wave * 1024), 16, 0, 0);
-        } else if (piece == 2) {
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(b_k + b_off[1]), FG_LDS(stB(st) + (wave + NWAVES) * 1024), 16, 0,
-                                             0);
+    // Load q of the wave's LOADS_PER_WAVE for K step kb into stage st: A instructions, then B, then the
+    // scale slice. `issue_piece(kb, st, i)` issues the i-th of MSUB near-equal pieces of that sequence.
+    auto issue_load = [&](int kb, int st, int q) {
+        if (q < C::UA) {
+            const uint8_t* a_k = a_tile + (int64_t)kb * BK;
+            __builtin_amdgcn_global_load_lds(FG_GLOBAL(a_k + a_off[q]), FG_LDS(stA(st) + a_t[q] * 1024), 16, 0, 0);
+        } else if (q < C::UA + C::UB) {
+            const int u = q - C::UA;
+            const uint8_t* b_k = B_TRANS ? b_tile + (int64_t)kb * BK * N : b_tile + (int64_t)kb * BK;
+            __builtin_amdgcn_global_load_lds(FG_GLOBAL(b_k + b_off[u]), FG_LDS(stB(st) + b_t[u] * 1024), 16, 0, 0);
         } else {
-            const bool rowb = SBK == SB_ROW && sc_wave >= 4;
-            const float* src = rowb ? SBp + (int64_t)kb * N + sc_row : p.sa + (int64_t)kb * p.sa_ld + sc_row;
-            float* dst = rowb ? stSB(st) + (sc_wave - 4) * 64 : stSA(st) + (sc_wave & 3) * 64;
-            if (!(SBK == SB_ROW) && sc_wave >= 4) {             // no per-row B scales: re-load an A slice
-                src = p.sa + (int64_t)kb * p.sa_ld + (m0 + (sc_wave & 3) * 64 + lane < p.sa_ld
-                                                          ? m0 + (sc_wave & 3) * 64 + lane : p.sa_ld - 1);
-                dst = stSA(st) + (sc_wave & 3) * 64;
-            }
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(src), FG_LDS(dst), 4, 0, 0);
+            const float* src = sc_is_b ? SBp + (int64_t)kb * N + sc_row : p.sa + (int64_t)kb * p.sa_ld + sc_row;
+            __builtin_amdgcn_global_load_lds(FG_GLOBAL(src), FG_LDS(reinterpret_cast<uint8_t*>(stSA(st)) + sc_dst), 4,
+                                             0, 0);
         }
     };
-    auto issue_loads = [&](int kb, int st) {
+    auto issue_piece = [&](int kb, int st, int piece) {
 #pragma unroll
-        for (int piece = 0; piece < 4; piece++) issue_piece(kb, st, piece);
+        for (int q = piece * C::LOADS_PER_WAVE / MSUB; q < (piece + 1) * C::LOADS_PER_WAVE / MSUB; q++)
+            issue_load(kb, st, q);
     };
 
     // ---------------- scale addressing ----------------
@@ -301,8 +328,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int h = 0; h < 4; h++) {
         const int crow = 32 * g16 + 8 * h + (lrow >> 1);
-        tr_off[h] = crow * 192 + 8 * (lrow & 1);
-        tr_z[h] = swzT(crow);
+        tr_off[h] = crow * BN + 8 * (lrow & 1);
+        tr_z[h] = swzT<BN>(crow);
     }
 
     // ---------------- main loop ----------------
@@ -310,7 +337,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     // of each step covers it and no step waits on a scale load of its own.
     float sb_next = 1.0f;
     if (nkb > 0) {
-        issue_loads(0, 0);
+#pragma unroll
+        for (int q = 0; q < C::LOADS_PER_WAVE; q++) issue_load(0, 0, q);
         sb_next = block_scale(0);
     }
     for (int kb = 0; kb < nkb; kb++) {
@@ -325,14 +353,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         const uint8_t* sAs = stA(st);
         const uint8_t* sBs = stB(st);
         const float* sSA = stSA(st);
-        // B-role fragments for the wave's 4 N tiles, held for the whole K step
+        // B-role fragments for the wave's NSUB N tiles, held for the whole K step
         v8i bf[NSUB];
 #pragma unroll
         for (int j = 0; j < NSUB; j++) {
             if constexpr (!B_TRANS) {
                 bf[j] = frag_at(sBs + (wn * WAVE_N + j * 16) * BK, frag_lo, frag_hi);
             } else {
-                const int chunk = wn * 4 + j;
+                const int chunk = wn * (WAVE_N / 16) + j;
                 v2i part[4];
 #pragma unroll
                 for (int h = 0; h < 4; h++)
@@ -340,12 +368,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                         (__attribute__((address_space(3))) v2i*)(sBs + tr_off[h] + ((chunk ^ tr_z[h]) << 4)));
                 bf[j] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
             }
-        }
-        float4 sbr[NSUB];
-        if constexpr (SBK == SB_ROW && !POW2) {
-            const float* sSB = stSB(st);
-#pragma unroll
-            for (int j = 0; j < NSUB; j++) sbr[j] = *reinterpret_cast<const float4*>(sSB + wn * WAVE_N + j * 16 + lcol4);
         }
         const uint8_t* sA_w = sAs + wm * WAVE_M * BK;
         const float* sSA_w = sSA + wm * WAVE_M + lrow;
@@ -370,44 +392,79 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                                                                                 ea);
             }
         } else {
-            // VALU promotion, software-pipelined by one MFMA: the FMAs that fold tile (i, j) into the FP32
-            // accumulators are issued after the MFMA of the next tile, so no FMA waits on the MFMA right
-            // before it (a VALU read of an MFMA result is not interlocked; the wait states would stall the
-            // wave). The scheduling groups pin the order: MFMA, then the previous tile's 4 FMAs.
-            v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
-            float s_prev[4] = {0.f, 0.f, 0.f, 0.f};
-            int ip = -1, jp = -1;
-            float sa_v[MSUB];
+            // VALU promotion, software-pipelined so that no FMA reads the result of the MFMA issued just
+            // before it (a VALU read of an MFMA result waits for the whole MFMA). With registers to spare
+            // (8-wave shape, one scale per lane) the FMAs that fold row i-1 into the FP32 accumulators
+            // follow the MFMAs of row i; otherwise the FMAs of each tile follow the next tile's MFMA.
+            constexpr bool ROW_PIPE = C::NW == 8 && SBK != SB_ROW;
+            float4 sbr[NSUB];
+            if constexpr (SBK == SB_ROW) {
+                const float* sSB = stSB(st);
 #pragma unroll
-            for (int i = 0; i < MSUB; i++) sa_v[i] = sSA_w[i * 16];
+                for (int j = 0; j < NSUB; j++)
+                    sbr[j] = *reinterpret_cast<const float4*>(sSB + wn * WAVE_N + j * 16 + lcol4);
+            }
+            if constexpr (ROW_PIPE) {
+                v4f prev[NSUB], cur[NSUB];
+                float sa_prev = 0.f;
 #pragma unroll
-            for (int i = 0; i < MSUB; i++) {
-                issue_piece(kb1, st ^ 1, i);
-                const v8i af = frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
+                for (int i = 0; i <= MSUB; i++) {
+                    float sa_i = 0.f;
+                    if (i < MSUB) {
+                        issue_piece(kb1, st ^ 1, i);
+                        const v8i af = frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
+                        sa_i = sSA_w[i * 16];
 #pragma unroll
-                for (int j = 0; j < NSUB; j++) {
-                    const v4f cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-                    if (ip >= 0) {
-#pragma unroll
-                        for (int r = 0; r < 4; r++) acc[ip][jp][r] = __builtin_fmaf(prev[r], s_prev[r], acc[ip][jp][r]);
+                        for (int j = 0; j < NSUB; j++)
+                            cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                                     0, 0, 0, 127, 0, 127);
                     }
-                    prev = cur;
-                    ip = i;
-                    jp = j;
-                    if constexpr (SBK != SB_ROW) {
-                        const float s_ij = sa_v[i] * sb_blk;
-                        s_prev[0] = s_prev[1] = s_prev[2] = s_prev[3] = s_ij;
-                    } else {
-                        s_prev[0] = sa_v[i] * sbr[j].x;
-                        s_prev[1] = sa_v[i] * sbr[j].y;
-                        s_prev[2] = sa_v[i] * sbr[j].z;
-                        s_prev[3] = sa_v[i] * sbr[j].w;
+                    if (i > 0) {
+                        const float s = sa_prev * sb_blk;
+#pragma unroll
+                        for (int j = 0; j < NSUB; j++)
+#pragma unroll
+                            for (int r = 0; r < 4; r++) acc[i - 1][j][r] = __builtin_fmaf(prev[j][r], s, acc[i - 1][j][r]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NSUB; j++) prev[j] = cur[j];
+                    sa_prev = sa_i;
+                }
+            } else {
+                v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
+                float s_prev[4] = {0.f, 0.f, 0.f, 0.f};
+                int ip = -1, jp = -1;
+#pragma unroll
+                for (int i = 0; i < MSUB; i++) {
+                    issue_piece(kb1, st ^ 1, i);
+                    const v8i af = frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
+                    const float sa_i = sSA_w[i * 16];
+#pragma unroll
+                    for (int j = 0; j < NSUB; j++) {
+                        const v4f cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bf[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                        if (ip >= 0) {
+#pragma unroll
+                            for (int r = 0; r < 4; r++)
+                                acc[ip][jp][r] = __builtin_fmaf(prev[r], s_prev[r], acc[ip][jp][r]);
+                        }
+                        prev = cur;
+                        ip = i;
+                        jp = j;
+                        if constexpr (SBK != SB_ROW) {
+                            const float s_ij = sa_i * sb_blk;
+                            s_prev[0] = s_prev[1] = s_prev[2] = s_prev[3] = s_ij;
+                        } else {
+                            s_prev[0] = sa_i * sbr[j].x;
+                            s_prev[1] = sa_i * sbr[j].y;
+                            s_prev[2] = sa_i * sbr[j].z;
+                            s_prev[3] = sa_i * sbr[j].w;
+                        }
                     }
                 }
-            }
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[ip][jp][r] = __builtin_fmaf(prev[r], s_prev[r], acc[ip][jp][r]);
+                for (int r = 0; r < 4; r++) acc[ip][jp][r] = __builtin_fmaf(prev[r], s_prev[r], acc[ip][jp][r]);
+            }
         }
     }
 
@@ -446,27 +503,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     }
 }
 
-template <bool B_TRANS, int SBK, bool GROUPED, bool POW2>
+template <class C, bool B_TRANS, int SBK, bool GROUPED, bool POW2>
 hipError_t launch_one(const GemmParams& p, unsigned grid, hipStream_t stream) {
-    auto kern = fg_gemm_kernel<B_TRANS, SBK, GROUPED, POW2>;
+    auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUPED, POW2>;
     static bool attr_set = false;   // benign race: setting the attribute twice is harmless
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), LDS_BYTES, stream, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NTHREADS), C::LDS_BYTES, stream, p);
     return hipGetLastError();
 }
 
-template <bool B_TRANS, int SBK, bool GROUPED>
-hipError_t launch(const GemmParams& p, unsigned grid, int pow2, hipStream_t stream) {
-    return pow2 ? launch_one<B_TRANS, SBK, GROUPED, true>(p, grid, stream)
-                : launch_one<B_TRANS, SBK, GROUPED, false>(p, grid, stream);
+template <class C>
+unsigned grid_for(const GemmParams& p, bool grouped) {
+    const int64_t n_tiles = (p.N + C::BN - 1) / C::BN;
+    const int64_t m_tiles = grouped ? (p.M + C::BM - 1) / C::BM + p.G : (p.M + C::BM - 1) / C::BM;
+    return (unsigned)(m_tiles * n_tiles);
 }
 
-unsigned tiles_2d(int64_t M, int64_t N) {
-    return (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+// Compute units of the current device (the tile count that fills one round).
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+// Workgroup shape for one launch: the one with the smaller estimated time, counting full rounds of tiles
+// over the compute units, a tile's work (BM * BN) and the measured per-tile rate of the 8-wave shape
+// (about 6% more MFMA throughput per CU). FG_GEMM_TILE=256x192 or 256x256 in the environment forces a
+// shape (tuning and tests).
+bool use_cfg8(const GemmParams& p, bool grouped) {
+    const char* force = getenv("FG_GEMM_TILE");
+    if (force && strcmp(force, "256x256") == 0) return true;
+    if (force && strcmp(force, "256x192") == 0) return false;
+    const int64_t cus = device_cus();
+    const int64_t r12 = (grid_for<Cfg12>(p, grouped) + cus - 1) / cus;
+    const int64_t r8 = (grid_for<Cfg8>(p, grouped) + cus - 1) / cus;
+    return (double)r8 * Cfg8::BM * Cfg8::BN / 1.06 < (double)r12 * Cfg12::BM * Cfg12::BN;
+}
+
+template <bool B_TRANS, int SBK, bool GROUPED>
+hipError_t launch(const GemmParams& p, int pow2, hipStream_t stream) {
+    if (use_cfg8(p, GROUPED)) {
+        const unsigned grid = grid_for<Cfg8>(p, GROUPED);
+        return pow2 ? launch_one<Cfg8, B_TRANS, SBK, GROUPED, true>(p, grid, stream)
+                    : launch_one<Cfg8, B_TRANS, SBK, GROUPED, false>(p, grid, stream);
+    }
+    const unsigned grid = grid_for<Cfg12>(p, GROUPED);
+    return pow2 ? launch_one<Cfg12, B_TRANS, SBK, GROUPED, true>(p, grid, stream)
+                : launch_one<Cfg12, B_TRANS, SBK, GROUPED, false>(p, grid, stream);
 }
 
 }  // namespace
@@ -476,7 +565,7 @@ hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_
     GemmParams p{};
     p.a = xq; p.sa = sx; p.sa_ld = M; p.b = wq; p.sb = sw;
     p.M = M; p.N = N; p.K = K; p.out = y; p.out_bf16 = out_bf16;
-    return launch<false, SB_BLOCK, false>(p, tiles_2d(M, N), pow2, stream);
+    return launch<false, SB_BLOCK, false>(p, pow2, stream);
 }
 
 hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
@@ -485,7 +574,7 @@ hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint
     GemmParams p{};
     p.a = dyq; p.sa = sdy; p.sa_ld = M; p.b = wq; p.sb = sw;
     p.M = M; p.N = K; p.K = N; p.out = dx; p.out_bf16 = out_bf16;
-    return launch<true, SB_BLOCK_T, false>(p, tiles_2d(M, K), pow2, stream);
+    return launch<true, SB_BLOCK_T, false>(p, pow2, stream);
 }
 
 hipError_t fg_launch_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
@@ -494,7 +583,7 @@ hipError_t fg_launch_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const ui
     GemmParams p{};
     p.a = dytq; p.sa = sdyt; p.sa_ld = N; p.b = xtq; p.sb = sxt;
     p.M = N; p.N = K; p.K = M; p.out = dw; p.out_bf16 = 0; p.accumulate = accumulate;
-    return launch<false, SB_ROW, false>(p, tiles_2d(N, K), pow2, stream);
+    return launch<false, SB_ROW, false>(p, pow2, stream);
 }
 
 hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
@@ -506,7 +595,5 @@ hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint
     p.offsets = offsets; p.G = G;
     p.b_group_stride = N * K;
     p.sb_group_stride = ((N + 127) / 128) * (K / 128);
-    const int64_t n_tiles = (N + BN - 1) / BN;
-    const int64_t m_tiles_max = (T + BM - 1) / BM + G;
-    return launch<false, SB_BLOCK, true>(p, (unsigned)(m_tiles_max * n_tiles), pow2, stream);
+    return launch<false, SB_BLOCK, true>(p, pow2, stream);
 }

@@ -48,6 +48,10 @@
  * adds 2^(ea+eb) * P_b straight into the FP32 accumulator, which is the same promotion with an exact
  * scale product and no VALU work. Passing FG_SCALE_POW2 with other scales gives unspecified results.
  *
+ * Every GEMM picks one of two workgroup tiles per launch (256x192 or 256x256 outputs) from the problem size
+ * and the device's compute-unit count; results agree to the same tolerance either way. The environment
+ * variable FG_GEMM_TILE=256x192 or FG_GEMM_TILE=256x256 forces one (read at every launch).
+ *
  * Layouts are row-major. "ld" arguments are row strides in elements.
  * Activation scales are MN-major: scale[group][row] (rows contiguous), so one 128-deep K step of a GEMM
  * reads its rows' scales as one contiguous run.

@@ -35,6 +35,21 @@ def _cmp(y_gpu, prom, bf16, tol_scale=1.0):
     return err
 
 
+# The library picks one of two workgroup shapes per launch (256x192 with 12 waves, 256x256 with 8 waves)
+# from the problem size; FG_GEMM_TILE forces one. Small shapes run under both, and under the automatic
+# choice; the full-size cases run under the automatic choice, the configuration the benchmark times.
+TILES = ["auto", "256x192", "256x256"]
+
+
+@pytest.fixture
+def tile(request, monkeypatch):
+    if request.param == "auto":
+        monkeypatch.delenv("FG_GEMM_TILE", raising=False)
+    else:
+        monkeypatch.setenv("FG_GEMM_TILE", request.param)
+    return request.param
+
+
 def _rand_act(rng, rows, cols, std=1.0):
     return wl.normal_bf16(rng, (rows, cols), std, outlier_channels=min(4, cols // 64), outlier_scale=20.0)
 
@@ -71,13 +86,15 @@ def test_fprop_tiny_config_fp32():
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (37, 130, 256), (256, 256, 128), (300, 520, 384),
                                    (513, 260, 640), (64, 1000, 1024), (1000, 64, 128)])
 @pytest.mark.parametrize("bf16", [False, True])
-def test_fprop_shapes(M, N, K, bf16):
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_fprop_shapes(M, N, K, bf16, tile):
     device()
     rng = np.random.default_rng(M * 31 + N * 7 + K)
     _fprop_case(_rand_act(rng, M, K), wl.normal_bf16(rng, (N, K), 0.02), bf16)
 
 
-def test_fprop_pow2_scales():
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_fprop_pow2_scales(tile):
     device()
     rng = np.random.default_rng(9)
     _fprop_case(_rand_act(rng, 200, 512), wl.normal_bf16(rng, (384, 512), 0.02), bf16=False, pow2=True)
@@ -155,7 +172,8 @@ def _dgrad_case(dy, w, bf16, pts=None, pow2=False):
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (37, 256, 128), (300, 384, 640), (256, 128, 256), (100, 512, 384)])
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("pow2", [False, True])
-def test_dgrad_shapes(M, N, K, bf16, pow2):
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_dgrad_shapes(M, N, K, bf16, pow2, tile):
     device()
     rng = np.random.default_rng(M * 13 + N * 5 + K)
     _dgrad_case(_rand_act(rng, M, N, 1e-3), wl.normal_bf16(rng, (N, K), 0.02), bf16, pow2=pow2)
@@ -197,14 +215,16 @@ def _wgrad_case(dy, x, pts=None, init=None, pow2=False):
 
 @pytest.mark.parametrize("M,N,K", [(128, 8, 8), (128, 40, 264), (256, 296, 384), (384, 256, 128), (512, 136, 72)])
 @pytest.mark.parametrize("pow2", [False, True])
-def test_wgrad_shapes(M, N, K, pow2):
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_wgrad_shapes(M, N, K, pow2, tile):
     device()
     rng = np.random.default_rng(M + N * 3 + K * 11)
     _wgrad_case(_rand_act(rng, M, N, 1e-3), _rand_act(rng, M, K), pow2=pow2)
 
 
 @pytest.mark.parametrize("pow2", [False, True])
-def test_wgrad_accumulate(pow2):
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_wgrad_accumulate(pow2, tile):
     device()
     rng = np.random.default_rng(5)
     M, N, K = 256, 200, 136
@@ -249,7 +269,8 @@ def _grouped_case(x, w, offsets, bf16=True, pts=None, pow2=False):
 
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("pow2", [False, True])
-def test_grouped_small_with_empty_groups(bf16, pow2):
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_grouped_small_with_empty_groups(bf16, pow2, tile):
     device()
     rng = np.random.default_rng(21)
     offsets = [0, 0, 300, 301, 301, 700, 957]            # empty groups at 0 and 3, a 1-row group
