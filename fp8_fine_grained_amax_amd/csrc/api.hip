@@ -73,11 +73,11 @@ fg_status fg_quantize_act_1x128(const void* x, int64_t rows, int64_t cols, int64
     const int pow2 = mode == FG_SCALE_POW2;
     if (axis == FG_ALONG_COLS) {
         if (cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-        if (cols / 128 > kMaxGridY || (rows + 63) / 64 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+        if ((cols / 128) * ((rows + 31) / 32) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
         return from_hip(fg_launch_quant_act_cols((const uint16_t*)x, rows, cols, ld_x, pow2, q, scales, stream));
     }
     if (rows % 128 != 0 || cols % 8 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-    if (rows / 128 > kMaxGridY || (cols + 63) / 64 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    if ((cols + 63) / 64 > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_quant_act_rows((const uint16_t*)x, rows, cols, ld_x, pow2, q, scales, stream));
 }
 

@@ -18,17 +18,20 @@
 // 1x128 tiles along columns.
 // One 1x128 bf16 tile is 256 B = 16 lanes x 16 B, i.e. exactly one DPP row, so the tile max-abs is four
 // DPP steps with no LDS. A 256-thread workgroup covers 16 rows of one 128-column group per unrolled
-// slot; blockIdx.y is the column group, so the 16 scales of a slot are one contiguous 64 B write in the
-// MN-major scale layout [cols/128][rows].
+// slot, and the 16 scales of a slot are one contiguous 64 B write in the MN-major scale layout
+// [cols/128][rows]. Workgroups are numbered column group first: the ones in flight together read whole
+// row segments of the same rows, which streams from HBM at the rate of a plain copy.
 // ------------------------------------------------------------------------------------------------
 template <int UNROLL>
 __global__ __launch_bounds__(256) void fg_quant_act_cols_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                                int64_t ld, int pow2, uint8_t* __restrict__ q,
-                                                                int64_t ldq, float* __restrict__ scales) {
+                                                                int64_t ld, int64_t groups, int pow2,
+                                                                uint8_t* __restrict__ q, int64_t ldq,
+                                                                float* __restrict__ scales) {
     const int lane16 = threadIdx.x & 15;
     const int slot = threadIdx.x >> 4;
-    const int64_t g = blockIdx.y;
-    const int64_t r_base = (int64_t)blockIdx.x * (16 * UNROLL) + slot;
+    const uint32_t bid = blockIdx.x, ng = (uint32_t)groups;
+    const int64_t g = bid % ng;
+    const int64_t r_base = (int64_t)(bid / ng) * (16 * UNROLL) + slot;
 
     uint4 v[UNROLL];
 #pragma unroll
@@ -45,14 +48,10 @@ __global__ __launch_bounds__(256) void fg_quant_act_cols_kernel(const uint16_t* 
         uint32_t m = fg_pk_max_u16(fg_pk_max_u16(v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu),
                                    fg_pk_max_u16(v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu));
         m = fg_max_halves(fg_row16_max_pk(m));
-        float s = fg_scale_from_amax_bits(m, pow2);
-        fg_divisor d = fg_make_divisor(s);
-        uint32_t lo = fg_cvt2<false>(fg_div(fg_bf16_lo(v[u].x), d), fg_div(fg_bf16_hi(v[u].x), d), 0);
-        lo = fg_cvt2<true>(fg_div(fg_bf16_lo(v[u].y), d), fg_div(fg_bf16_hi(v[u].y), d), lo);
-        uint32_t hi = fg_cvt2<false>(fg_div(fg_bf16_lo(v[u].z), d), fg_div(fg_bf16_hi(v[u].z), d), 0);
-        hi = fg_cvt2<true>(fg_div(fg_bf16_lo(v[u].w), d), fg_div(fg_bf16_hi(v[u].w), d), hi);
+        const float s = fg_scale_from_amax_bits(m, pow2);
+        const uint2 codes = fg_quant8_any(v[u], fg_make_divisor(s, pow2), pow2);
         if (r < rows) {
-            *reinterpret_cast<uint2*>(q + r * ldq + g * FG_GROUP + lane16 * 8) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(q + r * ldq + g * FG_GROUP + lane16 * 8) = codes;
             if (lane16 == 0) scales[g * rows + r] = s;
         }
     }
@@ -65,18 +64,22 @@ __global__ __launch_bounds__(256) void fg_quant_act_cols_kernel(const uint16_t* 
 // registers, then across the 8 lanes sharing a chunk with lane shuffles, then across the 4 waves in LDS.
 // Codes of one column and 4 consecutive rows pack into one dword (two cvt_pk per dword), go to an LDS
 // transpose buffer [64 cols][128 rows], and leave as 16 B stores: 128 contiguous bytes per column.
+// Workgroups are numbered row block first, so the ones in flight together extend the same output
+// columns: their 128 B pieces form contiguous runs of the transposed codes.
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fg_quant_act_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                 int64_t cols, int64_t ld, int pow2,
                                                                 uint8_t* __restrict__ q, float* __restrict__ scales) {
     __shared__ uint32_t colmax[4][32];          // [wave][column pair], packed u16 max-abs
+    __shared__ float col_s[64], col_r[64];      // per-column scale and reciprocal
+    __shared__ int any_tiny;
     __shared__ uint4 codes_t[64 * 8];           // [column][16 B piece], pieces swizzled per column
 
     const int t = threadIdx.x;
     const int chunk = t & 7;                    // 8-column chunk within the 64-column tile
     const int rgrp = t >> 3;                    // rows 4*rgrp .. 4*rgrp+3 within the 128-row tile
-    const int64_t r0 = (int64_t)blockIdx.y * FG_GROUP;
-    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)blockIdx.x * FG_GROUP;
+    const int64_t c0 = (int64_t)blockIdx.y * 64;
     const int64_t col = c0 + chunk * 8;
     const bool col_ok = col < cols;
 
@@ -109,36 +112,43 @@ __global__ __launch_bounds__(256) void fg_quant_act_rows_kernel(const uint16_t* 
         for (int p = 0; p < 4; p++) colmax[wave][chunk * 4 + p] = m[p];
     }
     __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-        m[p] = fg_pk_max_u16(fg_pk_max_u16(colmax[0][chunk * 4 + p], colmax[1][chunk * 4 + p]),
-                             fg_pk_max_u16(colmax[2][chunk * 4 + p], colmax[3][chunk * 4 + p]));
+    // One scale and reciprocal per column, computed once (wave 0, lane = column) and shared through LDS;
+    // the tile's 64 scales leave as one contiguous 256 B write.
+    if (wave == 0) {
+        const int c = t, pair = c >> 1;
+        const uint32_t mp = fg_pk_max_u16(fg_pk_max_u16(colmax[0][pair], colmax[1][pair]),
+                                          fg_pk_max_u16(colmax[2][pair], colmax[3][pair]));
+        const float s = fg_scale_from_amax_bits((c & 1) ? mp >> 16 : mp & 0xFFFFu, pow2);
+        const fg_divisor d = fg_make_divisor(s, pow2);
+        col_s[c] = d.s;
+        col_r[c] = d.r;
+        const uint64_t tiny = __builtin_amdgcn_ballot_w64(fg_divisor_tiny(d));
+        if (c == 0) any_tiny = tiny != 0;
+        if (c0 + c < cols) scales[(int64_t)blockIdx.x * cols + c0 + c] = s;
     }
-    float s[8];
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-        s[2 * p] = fg_scale_from_amax_bits(m[p] & 0xFFFFu, pow2);
-        s[2 * p + 1] = fg_scale_from_amax_bits(m[p] >> 16, pow2);
-    }
-    if (rgrp == 0 && col_ok) {
-        float* sp = scales + blockIdx.y * cols + col;
-#pragma unroll
-        for (int j = 0; j < 8; j++) sp[j] = s[j];
-    }
+    __syncthreads();
     // codes: dword j holds column chunk*8+j, rows 4*rgrp .. 4*rgrp+3 (byte i = row i)
     uint32_t* ct = reinterpret_cast<uint32_t*>(codes_t);
+    const int mode = pow2 ? FG_Q_POW2 : (any_tiny ? FG_Q_TINY : FG_Q_FAST);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        fg_divisor d = fg_make_divisor(s[j]);
+        const int c = chunk * 8 + j;
+        fg_divisor d{col_s[c], col_r[c]};
         float f[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             uint32_t w = (&v[i].x)[j >> 1];
-            f[i] = fg_div((j & 1) ? fg_bf16_hi(w) : fg_bf16_lo(w), d);
+            f[i] = (j & 1) ? fg_bf16_hi(w) : fg_bf16_lo(w);
         }
-        uint32_t dw = fg_cvt2<false>(f[0], f[1], 0);
-        dw = fg_cvt2<true>(f[2], f[3], dw);
-        const int c = chunk * 8 + j;
+        uint32_t dw;
+        if (mode == FG_Q_POW2) {
+            dw = fg_cvt2q<FG_Q_POW2, true>(f[2], f[3], d, fg_cvt2q<FG_Q_POW2, false>(f[0], f[1], d, 0));
+        } else if (mode == FG_Q_FAST || !fg_divisor_tiny(d)) {
+            dw = fg_cvt2q<FG_Q_FAST, true>(f[2], f[3], d, fg_cvt2q<FG_Q_FAST, false>(f[0], f[1], d, 0));
+        } else {
+            d = fg_divisor_shifted(d);
+            dw = fg_cvt2q<FG_Q_TINY, true>(f[2], f[3], d, fg_cvt2q<FG_Q_TINY, false>(f[0], f[1], d, 0));
+        }
         // dword rgrp of column c; the 16 B piece index (rgrp >> 2) is XOR-swizzled by (c >> 3) & 3
         const int piece = (rgrp >> 2) ^ ((c >> 3) & 3) * 2;
         ct[c * 32 + piece * 4 + (rgrp & 3)] = dw;
@@ -194,34 +204,32 @@ __global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restr
     uint32_t b = wmax[2] > wmax[3] ? wmax[2] : wmax[3];
     const float s = fg_scale_from_amax_bits(a > b ? a : b, pow2);
     if (t == 0) scales[blockIdx.y * kblocks + blockIdx.x] = s;
-    const fg_divisor d = fg_make_divisor(s);
+    const fg_divisor d = fg_make_divisor(s, pow2);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         int64_t r = r0 + rsub + 16 * i;
-        uint32_t lo = fg_cvt2<false>(fg_div(fg_bf16_lo(v[i].x), d), fg_div(fg_bf16_hi(v[i].x), d), 0);
-        lo = fg_cvt2<true>(fg_div(fg_bf16_lo(v[i].y), d), fg_div(fg_bf16_hi(v[i].y), d), lo);
-        uint32_t hi = fg_cvt2<false>(fg_div(fg_bf16_lo(v[i].z), d), fg_div(fg_bf16_hi(v[i].z), d), 0);
-        hi = fg_cvt2<true>(fg_div(fg_bf16_lo(v[i].w), d), fg_div(fg_bf16_hi(v[i].w), d), hi);
-        if (r < n) *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
+        const uint2 codes = fg_quant8_any(v[i], d, pow2);
+        if (r < n) *reinterpret_cast<uint2*>(q + r * ldq + c0) = codes;
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // Host launchers (arguments already validated by the C-ABI layer).
 // ------------------------------------------------------------------------------------------------
-constexpr int kActColsUnroll = 4;
+constexpr int kActColsUnroll = 2;
 
 hipError_t fg_launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
                                     uint8_t* q, float* scales, hipStream_t stream) {
-    dim3 grid((unsigned)((rows + 16 * kActColsUnroll - 1) / (16 * kActColsUnroll)), (unsigned)(cols / FG_GROUP));
-    hipLaunchKernelGGL(fg_quant_act_cols_kernel<kActColsUnroll>, grid, dim3(256), 0, stream, x, rows, ld, pow2, q,
-                       cols, scales);
+    const int64_t groups = cols / FG_GROUP;
+    const int64_t row_blocks = (rows + 16 * kActColsUnroll - 1) / (16 * kActColsUnroll);
+    hipLaunchKernelGGL(fg_quant_act_cols_kernel<kActColsUnroll>, dim3((unsigned)(groups * row_blocks)), dim3(256), 0,
+                       stream, x, rows, ld, groups, pow2, q, cols, scales);
     return hipGetLastError();
 }
 
 hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
                                     uint8_t* q, float* scales, hipStream_t stream) {
-    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(rows / FG_GROUP));
+    dim3 grid((unsigned)(rows / FG_GROUP), (unsigned)((cols + 63) / 64));
     hipLaunchKernelGGL(fg_quant_act_rows_kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, pow2, q, scales);
     return hipGetLastError();
 }
