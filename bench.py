@@ -8,7 +8,7 @@ One step = the whole hot path over one batch of the DeepSeek-V3-like dense MLP L
 `value` is the FP8 GEMM throughput of the whole step (3 x 2MNK FLOP over the step's wall time), with
 all inputs resident in HBM when the timed region starts. Per-kernel times come from HIP events on the
 stream the kernels run on. Also reported: per-kernel roofline fractions, cold-cache quantize bandwidth
-(a 1 GiB scrub between launches defeats the 256 MB Infinity Cache), the grouped MoE GEMM on one GPU's
+(a 1 GiB read between launches defeats the 256 MB Infinity Cache), the grouped MoE GEMM on one GPU's
 expert share, and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pow2] [--no-moe] [--no-cpu] [--no-cold] [--calib-copy]
@@ -57,6 +57,7 @@ def main():
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--no-vendor", action="store_true")
     ap.add_argument("--pow2", action="store_true", help="power-of-2 scales (quantizers round scales up to 2^k; "
                     "the GEMMs then apply them in the matrix core)")
     ap.add_argument("--calib-copy", action="store_true", help="only run a 512 MiB device copy (counter calibration)")
@@ -267,6 +268,12 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
 
+    # Context, not part of the path: the vendor library's FP8 GEMM (hipBLASLt through torch._scaled_mm, one
+    # scale per tensor, no fine-grained scaling or promotion) at the Fprop shape, same E4M3 format, BF16 out.
+    vendor = None
+    if not args.no_vendor:
+        vendor = vendor_reference(M, N, K, dev)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline()
@@ -292,10 +299,40 @@ def main():
                              for n, _, b, _ in alt_ops if b == "mfma"},
             "kernel_ms": {n: round(v, 4) for n, v in alt_per.items()}},
         "quantize_cold_cache": cold,
+        "vendor_fp8_gemm_reference": vendor,
         "moe_grouped": moe,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out))
+
+
+def vendor_reference(M, N, K, dev):
+    """hipBLASLt FP8 GEMM (torch._scaled_mm, per-tensor scales) on seeded N(0,1) E4M3 operands of the Fprop
+    shape: the throughput a plain FP8 GEMM reaches on this GPU, for context."""
+    import torch
+    try:
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        a = torch.randn((M, K), device=dev, generator=g).to(torch.float8_e4m3fn)
+        b = torch.randn((N, K), device=dev, generator=g).to(torch.float8_e4m3fn)
+        one = torch.tensor(1.0, device=dev)
+        run = lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        return {"what": "torch._scaled_mm (hipBLASLt) E4M3 x E4M3 -> BF16, per-tensor scales",
+                "shape": [M, N, K], "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+    except Exception as ex:                       # not available in this torch build
+        return {"error": repr(ex)[:200]}
 
 
 def cpu_baseline():
