@@ -45,6 +45,11 @@ def quant_bytes(rows, cols):
     return rows * cols * 3 + rows * cols // 128 * 4
 
 
+def quant_both_bytes(rows, cols):
+    """Both tilings from one read: 2 B in + 2 x 1 B out per element, two scales per 128 elements."""
+    return rows * cols * 4 + 2 * (rows * cols // 128) * 4
+
+
 def quant_w_bytes(n, k):
     return n * k * 3 + (n // 128) * (k // 128) * 4
 
@@ -110,7 +115,27 @@ def main():
     )
     B = bufs
 
-    def make_ops(pow2):
+    def make_ops(pow2, fused=True):
+        """The step's launches. fused: X and dY are read once each and quantized in both tilings (rows for
+        Fprop/Dgrad, tokens for Wgrad) by fg_quantize_act_1x128_both; otherwise each tiling has its own
+        launch."""
+        if fused:
+            return [
+                ("quant_x_both", lambda: fg.fg_quantize_act_1x128_both(x, pow2=pow2, q_cols=B["xq"], scales_cols=B["sx"],
+                                                                       q_rows=B["xtq"], scales_rows=B["sxt"]),
+                 "hbm", quant_both_bytes(M, K)),
+                ("quant_w_128x128", lambda: fg.fg_quantize_w_128x128(w, q=B["wq"], scales=B["sw"], pow2=pow2),
+                 "hbm", quant_w_bytes(N, K)),
+                ("fprop", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=pow2),
+                 "mfma", 2.0 * M * N * K),
+                ("quant_dy_both", lambda: fg.fg_quantize_act_1x128_both(dy, pow2=pow2, q_cols=B["dyq"], scales_cols=B["sdy"],
+                                                                        q_rows=B["dytq"], scales_rows=B["sdyt"]),
+                 "hbm", quant_both_bytes(M, N)),
+                ("dgrad", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"], pow2=pow2),
+                 "mfma", 2.0 * M * N * K),
+                ("wgrad", lambda: fg.fg_fp8_gemm_wgrad(B["dytq"], B["sdyt"], B["xtq"], B["sxt"], dw=B["dw"], pow2=pow2),
+                 "mfma", 2.0 * M * N * K),
+            ]
         return [
             ("quant_x_rowwise", lambda: fg.fg_quantize_act_1x128(x, q=B["xq"], scales=B["sx"], pow2=pow2),
              "hbm", quant_bytes(M, K)),
@@ -162,17 +187,28 @@ def main():
         return ms, per
 
     POW2 = bool(args.pow2)
-    ops = make_ops(POW2)
-    ms_per_step, per_kernel_ms = measure(ops, args.steps, args.warmup, "pow2 scales" if POW2 else "fp32 scales")
-    # The other scale mode, same buffers and shapes, reported beside the headline.
-    alt_ops = make_ops(not POW2)
-    alt_ms, alt_per = measure(alt_ops, args.steps, args.warmup, "fp32 scales" if POW2 else "pow2 scales")
+    ops = make_ops(POW2, fused=True)
+    ms_per_step, per_kernel_ms = measure(ops, args.steps, args.warmup,
+                                         ("pow2" if POW2 else "fp32") + " scales, fused quantizers")
+    # Other variants of the same step on the same buffers, reported beside the headline: the other scale
+    # mode, and one launch per tiling instead of the fused quantizers.
+    variants = {}
+    sep_ops, sep_per = None, None
+    for pw, fu in ((not POW2, True), (POW2, False), (not POW2, False)):
+        vops = make_ops(pw, fused=fu)
+        vms, vper = measure(vops, args.steps, args.warmup, ("pow2" if pw else "fp32") + " scales, " +
+                            ("fused quantizers" if fu else "separate quantizers"))
+        variants[("pow2" if pw else "fp32") + ("_fused" if fu else "_separate")] = (vops, vms, vper)
+        if pw == POW2 and not fu:
+            sep_ops, sep_per = vops, vper
 
     gemm_flop = 3 * 2.0 * M * N * K
     value = gemm_flop / (ms_per_step * 1e-3) / 1e12
 
     kernels = {}
-    for name, _, bound, work in ops:
+    for name, _, bound, work in ops + [o for o in sep_ops if o[2] == "hbm" and o[0] not in per_kernel_ms]:
+        if name not in per_kernel_ms:
+            per_kernel_ms[name] = sep_per[name]
         ms = per_kernel_ms[name]
         if bound == "mfma":
             ach = work / (ms * 1e-3) / 1e12
@@ -188,7 +224,7 @@ def main():
     if not args.no_cold:
         scrub = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         sink = torch.empty((), dtype=torch.int32, device=dev)
-        for name, fn, bound, work in ops:
+        for name, fn, bound, work in ops + [o for o in sep_ops if o[2] == "hbm" and o[0] != "quant_w_128x128"]:
             if bound != "hbm":
                 continue
             times = []
@@ -286,18 +322,18 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": "dsv3_dense_mlp_linear_fwd_bwd", "M_tokens": M, "N_out": N, "K_in": K,
-                   "tiles": "1x128 activations, 128x128 weights", "scale_mode": "pow2" if POW2 else "fp32", "accumulate": "fp32, promoted every 128 K",
+                   "tiles": "1x128 activations, 128x128 weights", "scale_mode": "pow2" if POW2 else "fp32",
+                   "quantizers": "fused (X and dY read once for both tilings)", "accumulate": "fp32, promoted every 128 K",
                    "fprop_out": "bf16", "dgrad_out": "f32", "wgrad_out": "f32"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "quantize_GBps_in_step": round(qbytes / (qms * 1e-3) / 1e9, 1),
         "kernels": kernels,
-        "other_scale_mode": {
-            "scale_mode": "fp32" if POW2 else "pow2", "ms_per_step": round(alt_ms, 4),
-            "value": round(gemm_flop / (alt_ms * 1e-3) / 1e12, 2),
-            "gemm_TFLOP/s": {n: round(2.0 * M * N * K / (alt_per[n] * 1e-3) / 1e12, 1)
-                             for n, _, b, _ in alt_ops if b == "mfma"},
-            "kernel_ms": {n: round(v, 4) for n, v in alt_per.items()}},
+        "variants": {k: {"ms_per_step": round(vms, 4), "value": round(gemm_flop / (vms * 1e-3) / 1e12, 2),
+                         "gemm_TFLOP/s": {n: round(2.0 * M * N * K / (vper[n] * 1e-3) / 1e12, 1)
+                                          for n, _, b, _ in vops if b == "mfma"},
+                         "kernel_ms": {n: round(v, 4) for n, v in vper.items()}}
+                     for k, (vops, vms, vper) in variants.items()},
         "quantize_cold_cache": cold,
         "vendor_fp8_gemm_reference": vendor,
         "moe_grouped": moe,

@@ -34,11 +34,12 @@ def lib():
         P, I64, I, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int32
         L.fg_quantize_act_1x128.argtypes = [P, I64, I64, I64, I, I, P, P, P]
         L.fg_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P, P]
+        L.fg_quantize_act_1x128_both.argtypes = [P, I64, I64, I64, I, P, P, P, P, P]
         L.fg_fp8_gemm_fprop.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_gemm_wgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
-        for f in ("fg_quantize_act_1x128", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop", "fg_fp8_gemm_dgrad",
+        for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop", "fg_fp8_gemm_dgrad",
                   "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm"):
             getattr(L, f).restype = I
         L.fg_status_string.argtypes = [I]
@@ -103,6 +104,29 @@ def fg_quantize_act_1x128(x, axis: int = FG_ALONG_COLS, pow2: bool = False, q=No
                                        FG_SCALE_POW2 if pow2 else FG_SCALE_FP32, _ptr(q), _ptr(scales),
                                        _stream(x.device)), "fg_quantize_act_1x128")
     return q, scales
+
+
+def fg_quantize_act_1x128_both(x, pow2: bool = False, q_cols=None, scales_cols=None, q_rows=None, scales_rows=None):
+    """Both 1x128 tilings of a bf16 [rows, cols] matrix from one read: returns (q_cols [rows, cols],
+    scales_cols [cols/128, rows], q_rows [cols, rows], scales_rows [rows/128, cols]), identical to
+    fg_quantize_act_1x128 with FG_ALONG_COLS and with FG_ALONG_ROWS."""
+    _gpu(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise Fp8fgError("x must be a 2-D bf16 tensor with unit column stride")
+    rows, cols = x.shape
+    dev = x.device
+    if q_cols is None:
+        q_cols = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scales_cols is None:
+        scales_cols = torch.empty(((cols + 127) // 128, rows), dtype=torch.float32, device=dev)
+    if q_rows is None:
+        q_rows = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if scales_rows is None:
+        scales_rows = torch.empty(((rows + 127) // 128, cols), dtype=torch.float32, device=dev)
+    _check(lib().fg_quantize_act_1x128_both(_ptr(x), rows, cols, x.stride(0), FG_SCALE_POW2 if pow2 else FG_SCALE_FP32,
+                                            _ptr(q_cols), _ptr(scales_cols), _ptr(q_rows), _ptr(scales_rows),
+                                            _stream(dev)), "fg_quantize_act_1x128_both")
+    return q_cols, scales_cols, q_rows, scales_rows
 
 
 def fg_quantize_w_128x128(w, pow2: bool = False, q=None, scales=None):

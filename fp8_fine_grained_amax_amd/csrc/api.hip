@@ -11,6 +11,8 @@ hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t col
                                     uint8_t* q, float* scales, hipStream_t stream);
 hipError_t fg_launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ld, int pow2, uint8_t* q,
                              float* scales, hipStream_t stream);
+hipError_t fg_launch_quant_act_both(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
+                                    uint8_t* qc, float* sc, uint8_t* qr, float* sr, hipStream_t stream);
 hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
                                 int64_t N, int64_t K, void* y, int out_bf16, int pow2, hipStream_t stream);
 hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
@@ -79,6 +81,21 @@ fg_status fg_quantize_act_1x128(const void* x, int64_t rows, int64_t cols, int64
     if (rows % 128 != 0 || cols % 8 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
     if ((cols + 63) / 64 > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_quant_act_rows((const uint16_t*)x, rows, cols, ld_x, pow2, q, scales, stream));
+}
+
+fg_status fg_quantize_act_1x128_both(const void* x, int64_t rows, int64_t cols, int64_t ld_x, fg_scale_mode mode,
+                                     uint8_t* q_cols, float* scales_cols, uint8_t* q_rows, float* scales_rows,
+                                     hipStream_t stream) {
+    if (rows < 0 || cols < 0 || !valid_mode(mode) || ld_x < cols) return FG_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return FG_OK;
+    if (!x || !q_cols || !scales_cols || !q_rows || !scales_rows) return FG_ERR_INVALID_ARG;
+    if (rows % 128 != 0 || cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(x) || !aligned16(q_cols) || !aligned16(q_rows) || !aligned4(scales_cols) || !aligned4(scales_rows) ||
+        (ld_x % 8) != 0)
+        return FG_ERR_MISALIGNED;
+    if (cols / 128 > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    return from_hip(fg_launch_quant_act_both((const uint16_t*)x, rows, cols, ld_x, mode == FG_SCALE_POW2, q_cols,
+                                             scales_cols, q_rows, scales_rows, stream));
 }
 
 fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_w, fg_scale_mode mode, uint8_t* q,

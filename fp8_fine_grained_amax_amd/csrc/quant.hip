@@ -214,6 +214,121 @@ __global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restr
 }
 
 // ------------------------------------------------------------------------------------------------
+// Both 1x128 tilings from one read: the codes and scales of FG_ALONG_COLS (tiles along the channels, as
+// the Fprop/Dgrad operand) and of FG_ALONG_ROWS (tiles along the tokens, transposed, as the Wgrad
+// operand). A 256-thread workgroup owns a 128 x 128 block: thread t holds rows 8*(t/16)+i (i = 0..7) of
+// the 8-column chunk t%16, so the 16 lanes of a DPP row hold one full 128-column row (row max-abs by DPP)
+// and the lanes sharing a chunk hold one column (column max-abs by lane shuffles and a 4-wave LDS
+// exchange). Row-tile codes leave directly (128 contiguous bytes per row); column-tile codes go through
+// an LDS transpose buffer [128 columns][128 rows] whose 16 B pieces are XOR-swizzled by column.
+// The bf16 block is read once instead of twice.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fg_quant_act_both_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t ld, int pow2,
+                                                                uint8_t* __restrict__ qc, float* __restrict__ sc,
+                                                                uint8_t* __restrict__ qr, float* __restrict__ sr) {
+    __shared__ uint32_t colmax[4][64];          // [wave][column pair], packed u16 max-abs
+    __shared__ float col_s[128], col_r[128];    // per-column scale and reciprocal
+    __shared__ int tiny_w[2];                   // per wave of the column-scale step: a scale below 2^-100
+    __shared__ uint4 codes_t[128 * 8];          // [column][16 B piece], pieces swizzled per column
+
+    const int t = threadIdx.x;
+    const int chunk = t & 15;                   // 8-column chunk within the 128-column block
+    const int rgrp = t >> 4;                    // rows 8*rgrp .. 8*rgrp+7 within the 128-row block
+    const int wave = t >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * FG_GROUP;
+    const int64_t c0 = (int64_t)blockIdx.y * FG_GROUP;
+    const int64_t g = blockIdx.y;               // column group of the row tiles
+
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = *reinterpret_cast<const uint4*>(x + (r0 + 8 * rgrp + i) * ld + c0 + chunk * 8);
+
+    // column max-abs (packed pairs): 8 rows in registers, the 4 lanes of a wave sharing the chunk, 4 waves
+    uint32_t m[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        m[p] = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) m[p] = fg_pk_max_u16(m[p], (&v[i].x)[p] & 0x7FFF7FFFu);
+        m[p] = fg_pk_max_u16(m[p], (uint32_t)__shfl_xor((int)m[p], 16));
+        m[p] = fg_pk_max_u16(m[p], (uint32_t)__shfl_xor((int)m[p], 32));
+    }
+    if ((t & 63) < 16) {
+#pragma unroll
+        for (int p = 0; p < 4; p++) colmax[wave][chunk * 4 + p] = m[p];
+    }
+
+    // row tiles: max-abs over the 16 lanes of the DPP row, codes straight out
+    float s_row[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        uint32_t mr = fg_pk_max_u16(fg_pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu),
+                                    fg_pk_max_u16(v[i].z & 0x7FFF7FFFu, v[i].w & 0x7FFF7FFFu));
+        mr = fg_max_halves(fg_row16_max_pk(mr));
+        s_row[i] = fg_scale_from_amax_bits(mr, pow2);
+        const uint2 codes = fg_quant8_any(v[i], fg_make_divisor(s_row[i], pow2), pow2);
+        *reinterpret_cast<uint2*>(qc + (r0 + 8 * rgrp + i) * cols + c0 + chunk * 8) = codes;
+    }
+    // lane `chunk` < 8 of each DPP row writes the scale of row 8*rgrp + chunk: 32 contiguous bytes
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        if (chunk == i) sc[g * rows + r0 + 8 * rgrp + i] = s_row[i];
+
+    __syncthreads();
+    // column tiles: one scale and reciprocal per column, shared through LDS
+    if (t < 128) {
+        const int c = t, pair = c >> 1;
+        const uint32_t mp = fg_pk_max_u16(fg_pk_max_u16(colmax[0][pair], colmax[1][pair]),
+                                          fg_pk_max_u16(colmax[2][pair], colmax[3][pair]));
+        const float s = fg_scale_from_amax_bits((c & 1) ? mp >> 16 : mp & 0xFFFFu, pow2);
+        const fg_divisor d = fg_make_divisor(s, pow2);
+        col_s[c] = d.s;
+        col_r[c] = d.r;
+        const uint64_t tiny = __builtin_amdgcn_ballot_w64(fg_divisor_tiny(d));
+        if ((c & 63) == 0) tiny_w[c >> 6] = tiny != 0;
+        sr[(int64_t)blockIdx.x * cols + c0 + c] = s;
+    }
+    __syncthreads();
+    const int mode = pow2 ? FG_Q_POW2 : ((tiny_w[0] | tiny_w[1]) ? FG_Q_TINY : FG_Q_FAST);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int c = chunk * 8 + j;
+        fg_divisor d{col_s[c], col_r[c]};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t w = (&v[i].x)[j >> 1];
+            f[i] = (j & 1) ? fg_bf16_hi(w) : fg_bf16_lo(w);
+        }
+        uint32_t d0, d1;
+        if (mode == FG_Q_POW2) {
+            d0 = fg_cvt2q<FG_Q_POW2, true>(f[2], f[3], d, fg_cvt2q<FG_Q_POW2, false>(f[0], f[1], d, 0));
+            d1 = fg_cvt2q<FG_Q_POW2, true>(f[6], f[7], d, fg_cvt2q<FG_Q_POW2, false>(f[4], f[5], d, 0));
+        } else if (mode == FG_Q_FAST || !fg_divisor_tiny(d)) {
+            d0 = fg_cvt2q<FG_Q_FAST, true>(f[2], f[3], d, fg_cvt2q<FG_Q_FAST, false>(f[0], f[1], d, 0));
+            d1 = fg_cvt2q<FG_Q_FAST, true>(f[6], f[7], d, fg_cvt2q<FG_Q_FAST, false>(f[4], f[5], d, 0));
+        } else {
+            d = fg_divisor_shifted(d);
+            d0 = fg_cvt2q<FG_Q_TINY, true>(f[2], f[3], d, fg_cvt2q<FG_Q_TINY, false>(f[0], f[1], d, 0));
+            d1 = fg_cvt2q<FG_Q_TINY, true>(f[6], f[7], d, fg_cvt2q<FG_Q_TINY, false>(f[4], f[5], d, 0));
+        }
+        // rows 8*rgrp .. +7 of column c: the 8 B half (rgrp & 1) of 16 B piece rgrp >> 1, swizzled
+        const int piece = (rgrp >> 1) ^ (chunk & 7);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(codes_t) + c * 128 + piece * 16 + (rgrp & 1) * 8) =
+            make_uint2(d0, d1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        const int id = t + 256 * h;             // 1024 pieces: column id/8, logical piece id%8
+        const int c = id >> 3, p = id & 7;
+        const uint4 val = codes_t[c * 8 + (p ^ ((c >> 3) & 7))];
+        *reinterpret_cast<uint4*>(qr + (c0 + c) * rows + r0 + 16 * p) = val;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Host launchers (arguments already validated by the C-ABI layer).
 // ------------------------------------------------------------------------------------------------
 constexpr int kActColsUnroll = 2;
@@ -238,5 +353,12 @@ hipError_t fg_launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ld
                              float* scales, hipStream_t stream) {
     dim3 grid((unsigned)(k / FG_GROUP), (unsigned)((n + FG_GROUP - 1) / FG_GROUP));
     hipLaunchKernelGGL(fg_quant_w_kernel, grid, dim3(256), 0, stream, w, n, ld, k / FG_GROUP, pow2, q, k, scales);
+    return hipGetLastError();
+}
+
+hipError_t fg_launch_quant_act_both(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
+                                    uint8_t* qc, float* sc, uint8_t* qr, float* sr, hipStream_t stream) {
+    dim3 grid((unsigned)(rows / FG_GROUP), (unsigned)(cols / FG_GROUP));
+    hipLaunchKernelGGL(fg_quant_act_both_kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, pow2, qc, sc, qr, sr);
     return hipGetLastError();
 }

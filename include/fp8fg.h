@@ -97,6 +97,20 @@ fg_status fg_quantize_act_1x128(const void* x, int64_t rows, int64_t cols, int64
                                 fg_tile_axis axis, fg_scale_mode mode,
                                 uint8_t* q, float* scales, hipStream_t stream);
 
+/* Both 1x128 tilings of one activation from a single read ([W1] Figure 6 passage: activations are kept in
+ * FP8 for the backward pass, where the Wgrad GEMM consumes them tiled along the tokens; [W5] passage on
+ * the transposed reads that the backward pass needs): writes exactly what fg_quantize_act_1x128 writes
+ * with FG_ALONG_COLS into (q_cols, scales_cols) and with FG_ALONG_ROWS into (q_rows, scales_rows),
+ * bit for bit, reading x once instead of twice.
+ *   x       bf16 [rows][cols], row stride ld_x; rows % 128 == 0 and cols % 128 == 0.
+ *   q_cols  u8 [rows][cols], scales_cols f32 [cols/128][rows]   (tiles along the columns)
+ *   q_rows  u8 [cols][rows], scales_rows f32 [rows/128][cols]   (tiles along the rows, transposed)
+ *   Alignment: x, q_cols, q_rows 16-byte aligned; ld_x % 8 == 0; scales 4-byte aligned.
+ *   rows == 0 or cols == 0 is a no-op returning FG_OK. */
+fg_status fg_quantize_act_1x128_both(const void* x, int64_t rows, int64_t cols, int64_t ld_x, fg_scale_mode mode,
+                                     uint8_t* q_cols, float* scales_cols, uint8_t* q_rows, float* scales_rows,
+                                     hipStream_t stream);
+
 /* 128x128 weight-block quantization ([W2]/[W3]/[W4], Figure 7 (a): per 128 input channels per 128
  * output channels).
  *   w       bf16 [n][k], row stride ld_w; k % 128 == 0; any n >= 0 (a short last block row-group takes

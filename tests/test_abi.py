@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -57,6 +57,18 @@ def test_quantize_act_rejections(L):
     assert q(ODD, 4, 128, 128, 0, 0, A16, A16, None) == MISALIGNED         # x not 16 B aligned
     assert q(A16, 4, 128, 132, 0, 0, A16, A16, None) == MISALIGNED         # ld % 8
     assert q(A16, 0, 128, 128, 0, 0, None, None, None) == OK               # empty: no-op
+
+
+def test_quantize_both_rejections(L):
+    q = L.fg_quantize_act_1x128_both
+    assert q(A16, -1, 128, 128, 0, A16, A16, A16, A16, None) == INVALID     # negative rows
+    assert q(A16, 128, 128, 128, 4, A16, A16, A16, A16, None) == INVALID    # bad mode
+    assert q(A16, 128, 128, 64, 0, A16, A16, A16, A16, None) == INVALID     # ld < cols
+    assert q(A16, 128, 128, 128, 0, A16, A16, None, A16, None) == INVALID   # null transposed codes
+    assert q(A16, 100, 128, 128, 0, A16, A16, A16, A16, None) == SHAPE      # rows % 128
+    assert q(A16, 128, 136, 136, 0, A16, A16, A16, A16, None) == SHAPE      # cols % 128
+    assert q(A16, 128, 128, 128, 0, A16, A16, ODD, A16, None) == MISALIGNED
+    assert q(A16, 0, 128, 128, 0, None, None, None, None, None) == OK        # empty: no-op
 
 
 def test_quantize_w_rejections(L):

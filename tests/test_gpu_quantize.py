@@ -172,3 +172,62 @@ def test_deterministic_repeat(dsv3):
     q1, s1 = fg.fg_quantize_act_1x128(x)
     q2, s2 = fg.fg_quantize_act_1x128(x)
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+# ------------------------------------------------------------------------------------------------
+# Both tilings from one read (fg_quantize_act_1x128_both): bit-exact against the oracle's two tilings
+# ------------------------------------------------------------------------------------------------
+
+def _check_both(x_cpu, pow2, ld_pad=0):
+    xb = bits(x_cpu)
+    x = to_dev(x_cpu)
+    if ld_pad:
+        big = torch.zeros((x.shape[0], x.shape[1] + ld_pad), dtype=torch.bfloat16, device=x.device)
+        big[:, : x.shape[1]] = x
+        x = big[:, : x_cpu.shape[1]]
+    qc, sc, qr, sr = fg.fg_quantize_act_1x128_both(x, pow2=pow2)
+    torch.cuda.synchronize()
+    for axis, q, s in ((fg.FG_ALONG_COLS, qc, sc), (fg.FG_ALONG_ROWS, qr, sr)):
+        q_ref, s_ref = oracle.quantize_act_1x128(xb, axis, pow2)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), f"axis {axis}: scales differ"
+        bad = np.argwhere(np_u8(q) != q_ref)
+        assert bad.size == 0, f"axis {axis}: {len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_both_dsv3_activation_and_gradient(dsv3, pow2):
+    x, _, dy = dsv3
+    _check_both(x, pow2)
+    _check_both(dy, pow2)
+
+
+@pytest.mark.parametrize("rows,cols,ld_pad", [(128, 128, 0), (256, 384, 8), (384, 1024, 24)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_both_shapes_and_strides(rows, cols, ld_pad, pow2):
+    device()
+    rng = np.random.default_rng(rows * 7 + cols)
+    _check_both(wl.normal_bf16(rng, (rows, cols), 1.0, outlier_channels=3, outlier_scale=40.0), pow2, ld_pad)
+
+
+def test_both_special_values():
+    """Special rows (zeros, signed zeros, subnormals, extremes, ties, tiny scales) placed both as rows and,
+    transposed, as columns of one 256 x 128 block, so each edge case drives a row tile and a column tile."""
+    device()
+    t = _special_tiles()
+    a = np.zeros((128, 128), np.uint16)
+    a[: t.shape[0]] = t
+    x = np.concatenate([a, np.ascontiguousarray(a.T)])
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    for pow2 in (False, True):
+        _check_both(xt, pow2)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_both_every_finite_bf16_value(pow2):
+    device()
+    allb = np.arange(65536, dtype=np.uint32)
+    finite = allb[((allb >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    n = (finite.size // (128 * 128)) * 128 * 128
+    x = finite[:n].reshape(-1, 128)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    _check_both(xt, pow2)
