@@ -20,7 +20,7 @@
 //                     wave reads 25% fewer LDS bytes per MFMA, which also lowers the LDS power that
 //                     competes with the matrix cores for the chip's clock.
 // Operand tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging), double-buffered. The
-// next K step's loads are issued in pieces spread over the current step's MFMA rows. LDS rows are 16 B-chunk
+// next K step's loads are issued in pieces ahead of the current step's first MFMA rows. LDS rows are 16 B-chunk
 // swizzled so fragment reads are bank-conflict-free. The MFMA is issued with the B-role fragment first, so
 // each lane ends up with one output row m and four consecutive output columns n (8 B bf16 / 16 B fp32
 // stores).
@@ -269,10 +269,16 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                                              0, 0);
         }
     };
+    // Pieces go out ahead of the first F MFMA rows of the step (loads issued early have longer to land;
+    // loads spread out disturb the MFMA stream less). Measured per shape on the dense-MLP GEMMs:
+    // 256x192 Fprop: F = 2; 256x256 Dgrad (transposed B): F = 3; otherwise spread over all rows.
+    constexpr int F = C::NW == 12 ? 2 : (B_TRANS ? 3 : MSUB);
     auto issue_piece = [&](int kb, int st, int piece) {
+        if (piece < F) {
 #pragma unroll
-        for (int q = piece * C::LOADS_PER_WAVE / MSUB; q < (piece + 1) * C::LOADS_PER_WAVE / MSUB; q++)
-            issue_load(kb, st, q);
+            for (int q = piece * C::LOADS_PER_WAVE / F; q < (piece + 1) * C::LOADS_PER_WAVE / F; q++)
+                issue_load(kb, st, q);
+        }
     };
 
     // ---------------- scale addressing ----------------
