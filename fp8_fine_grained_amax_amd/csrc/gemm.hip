@@ -160,8 +160,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous range of
         // logical tiles so the tiles it runs at the same time share A and B panels in its own L2.
         if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-        // groups of 8 M tiles: tiles in flight together form a compact block of the output
-        const int GM = 8;
+        // groups of GM M tiles: tiles in flight together on an XCD form a compact block of the output (4 x 8
+        // tiles of 256x192 and 8 x 4 tiles of 256x256 are the near-square blocks; both measured best)
+        const int GM = C::NW == 12 ? 4 : 8;
         const int group = id / (GM * n_tiles);
         const int first_m = group * GM;
         const int gsz = min(m_tiles - first_m, GM);
@@ -271,8 +272,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     };
     // Pieces go out ahead of the first F MFMA rows of the step (loads issued early have longer to land;
     // loads spread out disturb the MFMA stream less). Measured per shape on the dense-MLP GEMMs:
-    // 256x192 Fprop: F = 2; 256x256 Dgrad (transposed B): F = 3; otherwise spread over all rows.
-    constexpr int F = C::NW == 12 ? 2 : (B_TRANS ? 3 : MSUB);
+    // 256x192: F = 2; 256x256 with 128x128 weight blocks (Fprop, Dgrad): F = 3; per-row B scales (Wgrad):
+    // spread over all rows.
+    constexpr int F = C::NW == 12 ? 2 : (SBK == SB_ROW ? MSUB : 3);
     auto issue_piece = [&](int kb, int st, int piece) {
         if (piece < F) {
 #pragma unroll
