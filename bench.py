@@ -287,6 +287,40 @@ def main():
                 gbps = quant_bytes(T, H) / (ms * 1e-3) / 1e9
                 res[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
         moe = {"workload": "moe_grouped_8experts_65536rows_hidden7168_inter2048", "rows_per_expert": d["rows"].tolist(), **res}
+        del xm, hm, wu, wd, xq, hq, wdq, wds, yu, yd, d
+
+        # The up-projection's backward on the same expert share (routed rows padded per expert to 128
+        # tokens): grouped Dgrad dX = dY . W_up[e] and grouped Wgrad dW_up[e] = dY^T X over each expert's
+        # tokens, after one fused quantization of dY and X (both tilings). FLOP count over the real rows.
+        b = wl.moe_backward_inputs()
+        Tp = int(b["offsets"][-1])
+        Treal = int(b["rows"].sum())
+        xb, dyb = b["x"].to(dev), b["dy"].to(dev)
+        offb = torch.from_numpy(b["offsets"]).to(dev)
+        xq2, sx2, xtq2, sxt2 = fg.fg_quantize_act_1x128_both(xb, pow2=POW2)
+        dyq2, sdy2, dytq2, sdyt2 = fg.fg_quantize_act_1x128_both(dyb, pow2=POW2)
+        dxb = torch.empty((Tp, H), dtype=f32, device=dev)
+        dwb = torch.empty((E, I, H), dtype=f32, device=dev)
+        for name, fn, flop in [
+            ("grouped_dgrad_up", lambda: fg.fg_fp8_grouped_gemm_dgrad(dyq2, sdy2, wuq, wus, offb, dx=dxb, pow2=POW2),
+             2.0 * Treal * I * H),
+            ("grouped_wgrad_up", lambda: fg.fg_fp8_grouped_gemm_wgrad(dytq2, sdyt2, xtq2, sxt2, offb, dw=dwb, pow2=POW2),
+             2.0 * Treal * I * H),
+        ]:
+            for _ in range(3):
+                fn()
+            times = []
+            for _ in range(10):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            ach = flop / (ms * 1e-3) / 1e12
+            moe[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4)}
+        moe["backward_padded_rows"] = Tp
         print("[bench] grouped MoE timings done", file=sys.stderr, flush=True)
 
     # Roofline of the dominant (longest) GEMM kernel of the step.

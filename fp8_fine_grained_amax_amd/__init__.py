@@ -39,8 +39,10 @@ def lib():
         L.fg_fp8_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_gemm_wgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
+        L.fg_fp8_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
+        L.fg_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop", "fg_fp8_gemm_dgrad",
-                  "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm"):
+                  "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm", "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad"):
             getattr(L, f).restype = I
         L.fg_status_string.argtypes = [I]
         L.fg_status_string.restype = ctypes.c_char_p
@@ -198,3 +200,37 @@ def fg_fp8_grouped_gemm(xq, sx, wq, sw, offsets, out_dtype=torch.bfloat16, y=Non
     _check(lib().fg_fp8_grouped_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(offsets), G, T, N, K, _ptr(y),
                                      _out_code(y.dtype), _mode(pow2), _stream(xq.device)), "fg_fp8_grouped_gemm")
     return y
+
+
+def fg_fp8_grouped_gemm_dgrad(dyq, sdy, wq, sw, offsets, out_dtype=torch.float32, dx=None, pow2: bool = False):
+    """Per group g: dX[off[g]:off[g+1]] = dY[off[g]:off[g+1]] . W[g]. dyq [T, N], wq [G, N, K]; offsets: device int32."""
+    _gpu(dyq, sdy, wq, sw, offsets, dx)
+    if offsets.dtype != torch.int32:
+        raise Fp8fgError("offsets must be int32")
+    T, N = dyq.shape
+    G, _, K = wq.shape
+    if dx is None:
+        dx = torch.empty((T, K), dtype=out_dtype, device=dyq.device)
+    _check(lib().fg_fp8_grouped_gemm_dgrad(_ptr(dyq), _ptr(sdy), _ptr(wq), _ptr(sw), _ptr(offsets), G, T, N, K, _ptr(dx),
+                                           _out_code(dx.dtype), _mode(pow2), _stream(dyq.device)),
+           "fg_fp8_grouped_gemm_dgrad")
+    return dx
+
+
+def fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, offsets, dw=None, accumulate: bool = False, pow2: bool = False):
+    """Per group g: dW[g] (+)= dY[tokens of g]^T . X[tokens of g] from token-dim quantized dYt [N, T] and
+    Xt [K, T]; every offset a multiple of 128. Returns dw f32 [G, N, K]."""
+    _gpu(dytq, sdyt, xtq, sxt, offsets, dw)
+    if offsets.dtype != torch.int32:
+        raise Fp8fgError("offsets must be int32")
+    N, T = dytq.shape
+    K = xtq.shape[0]
+    G = offsets.numel() - 1
+    if dw is None:
+        if accumulate:
+            raise Fp8fgError("accumulate needs an existing dw")
+        dw = torch.empty((G, N, K), dtype=torch.float32, device=dytq.device)
+    _check(lib().fg_fp8_grouped_gemm_wgrad(_ptr(dytq), _ptr(sdyt), _ptr(xtq), _ptr(sxt), _ptr(offsets), G, T, N, K,
+                                           _ptr(dw), int(bool(accumulate)), _mode(pow2), _stream(dytq.device)),
+           "fg_fp8_grouped_gemm_wgrad")
+    return dw

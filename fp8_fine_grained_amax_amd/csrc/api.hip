@@ -11,6 +11,12 @@ hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t col
                                     uint8_t* q, float* scales, hipStream_t stream);
 hipError_t fg_launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ld, int pow2, uint8_t* q,
                              float* scales, hipStream_t stream);
+hipError_t fg_launch_gemm_grouped_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
+                                        const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, void* dx,
+                                        int out_bf16, int pow2, hipStream_t stream);
+hipError_t fg_launch_gemm_grouped_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
+                                        const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, float* dw,
+                                        int accumulate, int pow2, hipStream_t stream);
 hipError_t fg_launch_quant_act_both(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
                                     uint8_t* qc, float* sc, uint8_t* qr, float* sr, hipStream_t stream);
 hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
@@ -153,6 +159,36 @@ fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t*
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_grouped(xq, sx, wq, sw, d_offsets, G, total_rows, N, K, y, out == FG_OUT_BF16,
                                            scales == FG_SCALE_POW2, stream));
+}
+
+fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
+                                    const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
+                                    void* dx, fg_out_dtype out, fg_scale_mode scales, hipStream_t stream) {
+    if (G < 1 || G > kMaxGroups || total_rows < 0 || N < 0 || K < 0 || !valid_out(out) || !valid_mode(scales))
+        return FG_ERR_INVALID_ARG;
+    if (total_rows == 0 || K == 0) return FG_OK;
+    if (!dx || !d_offsets || (N > 0 && (!dyq || !sdy || !wq || !sw))) return FG_ERR_INVALID_ARG;
+    if (N % 128 != 0 || K % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (((total_rows + 255) / 256 + G) * ((K + 127) / 128) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(dyq) || !aligned16(wq) || !aligned16(dx) || !aligned4(sdy) || !aligned4(sw) || !aligned4(d_offsets))
+        return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_gemm_grouped_dgrad(dyq, sdy, wq, sw, d_offsets, G, total_rows, N, K, dx, out == FG_OUT_BF16,
+                                                 scales == FG_SCALE_POW2, stream));
+}
+
+fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
+                                    const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
+                                    float* dw, int accumulate, fg_scale_mode scales, hipStream_t stream) {
+    if (G < 1 || G > kMaxGroups || total_rows < 0 || N < 0 || K < 0 || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
+    if (N == 0 || K == 0) return FG_OK;
+    if (!dw || !d_offsets || (total_rows > 0 && (!dytq || !sdyt || !xtq || !sxt))) return FG_ERR_INVALID_ARG;
+    if (total_rows % 128 != 0 || K % 4 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (tiles(N, K) * G > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(dytq) || !aligned16(xtq) || !aligned16(dw) || !aligned16(sxt) || !aligned4(sdyt) ||
+        !aligned4(d_offsets))
+        return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_gemm_grouped_wgrad(dytq, sdyt, xtq, sxt, d_offsets, G, total_rows, N, K, dw,
+                                                 accumulate != 0, scales == FG_SCALE_POW2, stream));
 }
 
 }  // extern "C"

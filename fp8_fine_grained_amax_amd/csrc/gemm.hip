@@ -32,7 +32,10 @@
 //   SB_BLOCK  sB = sw[n/128][b]           (Fprop / grouped: 128x128 weight blocks)
 //   SB_BLOCK_T sB = sw[b][n/128]          (Dgrad: the same blocks, read along the other axis)
 //   SB_ROW    sB = sb[b][n]               (Wgrad: 1x128 tiles along tokens on both operands)
-//   GROUPED   rows split into per-group segments given by device offsets, B and sB per group.
+//   GRP_ROWS  rows split into per-group segments given by device offsets, B and sB per group (grouped
+//             Fprop, grouped Dgrad of the MoE experts).
+//   GRP_K     the contraction split into per-group token segments given by device offsets (multiples of
+//             128), one output matrix per group (grouped Wgrad of the MoE experts).
 #include <stdlib.h>
 #include <string.h>
 
@@ -68,6 +71,7 @@ using Cfg12 = TileCfg<4, 3, 64, 64>;   // 256 x 192
 using Cfg8 = TileCfg<2, 4, 128, 64>;   // 256 x 256
 
 enum { SB_BLOCK = 0, SB_BLOCK_T = 1, SB_ROW = 2 };
+enum { GRP_NONE = 0, GRP_ROWS = 1, GRP_K = 2 };
 
 struct GemmParams {
     const uint8_t* a;       // A-role codes [rows][K], row stride K
@@ -83,6 +87,7 @@ struct GemmParams {
     int G;
     int64_t b_group_stride; // elements between consecutive groups' B
     int64_t sb_group_stride;
+    int64_t out_group_stride; // GRP_K: elements between consecutive groups' outputs
 };
 
 // LDS swizzles. gfx950 serves a ds_read_b128 16 lanes (256 B, all 64 banks) at a time, and the 8 rows
@@ -116,7 +121,7 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* tile16, int lo_off, int hi
 // E8M0 code of an fp32 power of two in [2^-127, 2^127]: its biased exponent field.
 __device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23) & 0xFF; }
 
-template <class C, bool B_TRANS, int SBK, bool GROUPED, bool POW2>
+template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2>
 __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     constexpr int BM = C::BM, BN = C::BN, NW = C::NW, MSUB = C::MSUB, NSUB = C::NSUB;
     constexpr int WAVE_M = C::WAVE_M, WAVE_N = C::WAVE_N;
@@ -128,14 +133,37 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     const int64_t N = p.N, K = p.K;
     const int64_t lda = K;
     const bool vec_ok = (N & 3) == 0;       // output rows are 16 B (fp32) / 8 B (bf16) aligned
-    const int nkb = (int)(K / BK);
+    const int nkb_all = (int)(K / BK);      // 128-blocks of the whole contraction (block-scale layout)
+    int nkb = nkb_all;                      // K steps of this tile
 
     // ---------------- tile assignment ----------------
     int64_t m0, m_end, n0;
+    const uint8_t* Ap = p.a;
     const uint8_t* Bp = p.b;
+    const float* SAp = p.sa;
     const float* SBp = p.sb;
+    void* outp = p.out;
     const int n_tiles = (int)((N + BN - 1) / BN);
-    if constexpr (GROUPED) {
+    if constexpr (GROUP == GRP_K) {
+        // tile id = g * (tiles per group) + local tile; the group's token segment [off[g], off[g+1]) is the
+        // contraction, a whole number of 128-blocks
+        const int m_tiles = (int)((p.M + BM - 1) / BM);
+        const int tpg = m_tiles * n_tiles;
+        const int g = blockIdx.x / tpg;
+        const int local = blockIdx.x % tpg;
+        const int64_t seg0 = p.offsets[g], seg1 = p.offsets[g + 1];
+        const int64_t kb0 = seg0 / BK;
+        nkb = (int)((seg1 - seg0) / BK);
+        const int mt = local % m_tiles, nt = local / m_tiles;
+        m0 = (int64_t)mt * BM;
+        m_end = p.M;
+        n0 = (int64_t)nt * BN;
+        Ap += kb0 * BK;
+        Bp += kb0 * BK;
+        SAp += kb0 * p.sa_ld;
+        SBp += kb0 * N;
+        outp = reinterpret_cast<float*>(p.out) + (int64_t)g * p.out_group_stride;
+    } else if constexpr (GROUP == GRP_ROWS) {
         const int id_m = blockIdx.x / n_tiles;
         const int nt = blockIdx.x % n_tiles;
         int g = 0, cum = 0;
@@ -189,7 +217,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     // which keeps every wave's issue sequence identical and branch-free.
     // Lane l lands at row 8t + l/8, physical chunk l%8, and fetches logical chunk (l%8) ^ swz128(row).
     // Offsets are relative to wave-uniform tile bases (SGPRs) and fit in 32 bits.
-    const uint8_t* a_tile = p.a + m0 * lda;
+    const uint8_t* a_tile = Ap + m0 * lda;
     uint32_t a_off[C::UA];
     int a_t[C::UA];
 #pragma unroll
@@ -265,7 +293,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
             const uint8_t* b_k = B_TRANS ? b_tile + (int64_t)kb * BK * N : b_tile + (int64_t)kb * BK;
             __builtin_amdgcn_global_load_lds(FG_GLOBAL(b_k + b_off[u]), FG_LDS(stB(st) + b_t[u] * 1024), 16, 0, 0);
         } else {
-            const float* src = sc_is_b ? SBp + (int64_t)kb * N + sc_row : p.sa + (int64_t)kb * p.sa_ld + sc_row;
+            const float* src = sc_is_b ? SBp + (int64_t)kb * N + sc_row : SAp + (int64_t)kb * p.sa_ld + sc_row;
             __builtin_amdgcn_global_load_lds(FG_GLOBAL(src), FG_LDS(reinterpret_cast<uint8_t*>(stSA(st)) + sc_dst), 4,
                                              0, 0);
         }
@@ -295,7 +323,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     int64_t nblk = wave_n0 / 128;                 // a 64-column wave tile never straddles a 128-block
     nblk = nblk < nblocks ? nblk : nblocks - 1;
     auto block_scale = [&](int kb) -> float {
-        if constexpr (SBK == SB_BLOCK) return SBp[nblk * nkb + kb];
+        if constexpr (SBK == SB_BLOCK) return SBp[nblk * nkb_all + kb];
         if constexpr (SBK == SB_BLOCK_T) return SBp[(int64_t)kb * nblocks + nblk];
         return 1.0f;
     };
@@ -307,7 +335,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < NSUB; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     if (p.accumulate) {
-        const float* o = reinterpret_cast<const float*>(p.out);
+        const float* o = reinterpret_cast<const float*>(outp);
 #pragma unroll
         for (int i = 0; i < MSUB; i++) {
             const int64_t m = m0 + wm * WAVE_M + i * 16 + lrow;
@@ -494,7 +522,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         for (int j = 0; j < NSUB; j++) {
             const int64_t n = wave_n0 + j * 16 + lcol4;
             if (p.out_bf16) {
-                uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * N + n;
+                uint16_t* o = reinterpret_cast<uint16_t*>(outp) + m * N + n;
                 if (vec_ok && n + 3 < N) {
                     uint2 v;
                     v.x = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
@@ -506,7 +534,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                         if (n + r < N) o[r] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
                 }
             } else {
-                float* o = reinterpret_cast<float*>(p.out) + m * N + n;
+                float* o = reinterpret_cast<float*>(outp) + m * N + n;
                 if (vec_ok && n + 3 < N) {
                     *reinterpret_cast<float4*>(o) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
                 } else {
@@ -519,9 +547,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     }
 }
 
-template <class C, bool B_TRANS, int SBK, bool GROUPED, bool POW2>
+template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2>
 hipError_t launch_one(const GemmParams& p, unsigned grid, hipStream_t stream) {
-    auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUPED, POW2>;
+    auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUP, POW2>;
     static bool attr_set = false;   // benign race: setting the attribute twice is harmless
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -533,9 +561,11 @@ hipError_t launch_one(const GemmParams& p, unsigned grid, hipStream_t stream) {
 }
 
 template <class C>
-unsigned grid_for(const GemmParams& p, bool grouped) {
+unsigned grid_for(const GemmParams& p, int group) {
     const int64_t n_tiles = (p.N + C::BN - 1) / C::BN;
-    const int64_t m_tiles = grouped ? (p.M + C::BM - 1) / C::BM + p.G : (p.M + C::BM - 1) / C::BM;
+    const int64_t m_tiles = (p.M + C::BM - 1) / C::BM;
+    if (group == GRP_ROWS) return (unsigned)((m_tiles + p.G) * n_tiles);   // worst case over the offsets
+    if (group == GRP_K) return (unsigned)(m_tiles * n_tiles * p.G);
     return (unsigned)(m_tiles * n_tiles);
 }
 
@@ -552,7 +582,7 @@ int device_cus() {
 // over the compute units, a tile's work (BM * BN) and the measured per-tile rate of the 8-wave shape
 // (about 6% more MFMA throughput per CU). FG_GEMM_TILE=256x192 or 256x256 in the environment forces a
 // shape (tuning and tests).
-bool use_cfg8(const GemmParams& p, bool grouped) {
+bool use_cfg8(const GemmParams& p, int grouped) {
     const char* force = getenv("FG_GEMM_TILE");
     if (force && strcmp(force, "256x256") == 0) return true;
     if (force && strcmp(force, "256x192") == 0) return false;
@@ -562,16 +592,16 @@ bool use_cfg8(const GemmParams& p, bool grouped) {
     return (double)r8 * Cfg8::BM * Cfg8::BN / 1.06 < (double)r12 * Cfg12::BM * Cfg12::BN;
 }
 
-template <bool B_TRANS, int SBK, bool GROUPED>
+template <bool B_TRANS, int SBK, int GROUP>
 hipError_t launch(const GemmParams& p, int pow2, hipStream_t stream) {
-    if (use_cfg8(p, GROUPED)) {
-        const unsigned grid = grid_for<Cfg8>(p, GROUPED);
-        return pow2 ? launch_one<Cfg8, B_TRANS, SBK, GROUPED, true>(p, grid, stream)
-                    : launch_one<Cfg8, B_TRANS, SBK, GROUPED, false>(p, grid, stream);
+    if (use_cfg8(p, GROUP)) {
+        const unsigned grid = grid_for<Cfg8>(p, GROUP);
+        return pow2 ? launch_one<Cfg8, B_TRANS, SBK, GROUP, true>(p, grid, stream)
+                    : launch_one<Cfg8, B_TRANS, SBK, GROUP, false>(p, grid, stream);
     }
-    const unsigned grid = grid_for<Cfg12>(p, GROUPED);
-    return pow2 ? launch_one<Cfg12, B_TRANS, SBK, GROUPED, true>(p, grid, stream)
-                : launch_one<Cfg12, B_TRANS, SBK, GROUPED, false>(p, grid, stream);
+    const unsigned grid = grid_for<Cfg12>(p, GROUP);
+    return pow2 ? launch_one<Cfg12, B_TRANS, SBK, GROUP, true>(p, grid, stream)
+                : launch_one<Cfg12, B_TRANS, SBK, GROUP, false>(p, grid, stream);
 }
 
 }  // namespace
@@ -581,7 +611,7 @@ hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_
     GemmParams p{};
     p.a = xq; p.sa = sx; p.sa_ld = M; p.b = wq; p.sb = sw;
     p.M = M; p.N = N; p.K = K; p.out = y; p.out_bf16 = out_bf16;
-    return launch<false, SB_BLOCK, false>(p, pow2, stream);
+    return launch<false, SB_BLOCK, GRP_NONE>(p, pow2, stream);
 }
 
 hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
@@ -590,7 +620,7 @@ hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint
     GemmParams p{};
     p.a = dyq; p.sa = sdy; p.sa_ld = M; p.b = wq; p.sb = sw;
     p.M = M; p.N = K; p.K = N; p.out = dx; p.out_bf16 = out_bf16;
-    return launch<true, SB_BLOCK_T, false>(p, pow2, stream);
+    return launch<true, SB_BLOCK_T, GRP_NONE>(p, pow2, stream);
 }
 
 hipError_t fg_launch_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
@@ -599,7 +629,7 @@ hipError_t fg_launch_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const ui
     GemmParams p{};
     p.a = dytq; p.sa = sdyt; p.sa_ld = N; p.b = xtq; p.sb = sxt;
     p.M = N; p.N = K; p.K = M; p.out = dw; p.out_bf16 = 0; p.accumulate = accumulate;
-    return launch<false, SB_ROW, false>(p, pow2, stream);
+    return launch<false, SB_ROW, GRP_NONE>(p, pow2, stream);
 }
 
 hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
@@ -611,5 +641,30 @@ hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint
     p.offsets = offsets; p.G = G;
     p.b_group_stride = N * K;
     p.sb_group_stride = ((N + 127) / 128) * (K / 128);
-    return launch<false, SB_BLOCK, true>(p, pow2, stream);
+    return launch<false, SB_BLOCK, GRP_ROWS>(p, pow2, stream);
+}
+
+hipError_t fg_launch_gemm_grouped_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
+                                        const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, void* dx,
+                                        int out_bf16, int pow2, hipStream_t stream) {
+    // per group g: dX[rows of g][K] = dY[rows of g][N] . W[g][N][K] (A-role dY, B-role W[g] read transposed)
+    GemmParams p{};
+    p.a = dyq; p.sa = sdy; p.sa_ld = T; p.b = wq; p.sb = sw;
+    p.M = T; p.N = K; p.K = N; p.out = dx; p.out_bf16 = out_bf16;
+    p.offsets = offsets; p.G = G;
+    p.b_group_stride = N * K;
+    p.sb_group_stride = (N / 128) * ((K + 127) / 128);
+    return launch<true, SB_BLOCK_T, GRP_ROWS>(p, pow2, stream);
+}
+
+hipError_t fg_launch_gemm_grouped_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
+                                        const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, float* dw,
+                                        int accumulate, int pow2, hipStream_t stream) {
+    // per group g: dW[g][N][K] (+)= dYt[N][tokens of g] . Xt[K][tokens of g]^T
+    GemmParams p{};
+    p.a = dytq; p.sa = sdyt; p.sa_ld = N; p.b = xtq; p.sb = sxt;
+    p.M = N; p.N = K; p.K = T; p.out = dw; p.out_bf16 = 0; p.accumulate = accumulate;
+    p.offsets = offsets; p.G = G;
+    p.out_group_stride = N * K;
+    return launch<false, SB_ROW, GRP_K>(p, pow2, stream);
 }

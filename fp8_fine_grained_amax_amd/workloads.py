@@ -115,3 +115,25 @@ def moe_inputs(seed=1005, rows_scale=1.0, hidden=MOE_HIDDEN, inter=MOE_INTER, ex
     w_up = normal_bf16(rng, (experts, inter, hidden), 0.006)
     w_down = normal_bf16(rng, (experts, hidden, inter), 0.006)
     return dict(rows=rows, offsets=offsets, x=x, h=h, w_up=w_up, w_down=w_down)
+
+
+def moe_backward_inputs(seed=1006, rows_scale=1.0, hidden=MOE_HIDDEN, inter=MOE_INTER, experts=MOE_EXPERTS, pad=128):
+    """The up-projection's backward on one GPU's expert share, in a routed layout whose expert segments are
+    padded with zero rows to multiples of `pad` tokens (so 1x128 token tiles never straddle two experts):
+    X [T, hidden] ~N(0, 1), the output gradient dY [T, inter] ~N(0, 1e-3), W_up [E, inter, hidden]
+    ~N(0, 0.006), and the padded offsets [E+1]. Same Zipf(1.1) routing skew as moe_rows."""
+    assignments = int(round(MOE_TOKENS * MOE_TOPK * rows_scale))
+    rows, _ = moe_rows(seed, experts, assignments)
+    padded = ((rows + pad - 1) // pad) * pad
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    T = int(offsets[-1])
+    rng = np.random.default_rng(seed + 1)
+    x = normal_bf16(rng, (T, hidden), 1.0)
+    dy = normal_bf16(rng, (T, inter), 1e-3)
+    keep = np.zeros(T, bool)
+    for e in range(experts):
+        keep[offsets[e]: offsets[e] + rows[e]] = True
+    x[torch.from_numpy(~keep)] = 0
+    dy[torch.from_numpy(~keep)] = 0
+    w_up = normal_bf16(rng, (experts, inter, hidden), 0.006)
+    return dict(rows=rows, offsets=offsets, x=x, dy=dy, w_up=w_up)

@@ -161,6 +161,29 @@ fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t*
                               int64_t N, int64_t K, void* y, fg_out_dtype out, fg_scale_mode scales,
                               hipStream_t stream);
 
+/* Grouped Dgrad of the routed experts (the backward of fg_fp8_grouped_gemm, the MoE backward pass of
+ * [W1]/[W5], Figure 6 applied per expert). For each group g:
+ *   dX[off[g]:off[g+1]][:] = dY[off[g]:off[g+1]][:] . W[g]
+ *   dyq u8 [T][N], sdy f32 [N/128][T]        (dY quantized FG_ALONG_COLS over all T rows)
+ *   wq  u8 [G][N][K], sw f32 [G][N/128][K/128] (the experts' weight codes and blocks, as in Fprop)
+ *   dx  [T][K] f32 or bf16.  N % 128 == 0, K % 128 == 0.
+ *   d_offsets: DEVICE int32 [G+1] as for fg_fp8_grouped_gemm (precondition, not re-checked). */
+fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
+                                    const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
+                                    void* dx, fg_out_dtype out, fg_scale_mode scales, hipStream_t stream);
+
+/* Grouped Wgrad of the routed experts: for each group g, over the group's tokens,
+ *   dW[g][N][K] (+)= dY[tokens of g][N]^T . X[tokens of g][K]
+ *   dytq u8 [N][T], sdyt f32 [T/128][N]   (dY quantized FG_ALONG_ROWS over all T tokens)
+ *   xtq  u8 [K][T], sxt  f32 [T/128][K]   (X quantized FG_ALONG_ROWS)
+ *   dw   f32 [G][N][K]; accumulate != 0 starts each element from the value already in dw.
+ *   The 1x128 token tiles must not straddle two groups: every d_offsets[g] is a multiple of 128 (a
+ *   routed layout padded per expert; precondition, not re-checked). T % 128 == 0, K % 4 == 0.
+ *   An empty group writes zeros (or leaves dw unchanged with accumulate). */
+fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
+                                    const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
+                                    float* dw, int accumulate, fg_scale_mode scales, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* fg_status_string(fg_status s);
 

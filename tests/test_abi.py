@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -98,6 +98,16 @@ def test_gemm_rejections(L):
     assert g(A16, A16, A16, A16, A16B, 0, 128, 128, 128, A16, 0, 0, None) == INVALID   # G < 1
     assert g(A16, A16, A16, A16, None, 2, 128, 128, 128, A16, 0, 0, None) == INVALID   # null offsets
     assert g(A16, A16, A16, A16, A16B, 2, 128, 128, 100, A16, 0, 0, None) == SHAPE     # K % 128
+    gd = L.fg_fp8_grouped_gemm_dgrad
+    assert gd(A16, A16, A16, A16, A16B, 0, 128, 128, 128, A16, 0, 0, None) == INVALID  # G < 1
+    assert gd(A16, A16, A16, A16, A16B, 2, 128, 100, 128, A16, 0, 0, None) == SHAPE    # N (contraction) % 128
+    assert gd(A16, A16, A16, A16, A16B, 2, 128, 128, 128, ODD, 0, 0, None) == MISALIGNED
+    assert gd(None, None, None, None, A16B, 2, 0, 128, 128, None, 0, 0, None) == OK    # empty
+    gw = L.fg_fp8_grouped_gemm_wgrad
+    assert gw(A16, A16, A16, A16, None, 2, 256, 128, 128, A16, 0, 0, None) == INVALID  # null offsets
+    assert gw(A16, A16, A16, A16, A16B, 2, 200, 128, 128, A16, 0, 0, None) == SHAPE    # tokens % 128
+    assert gw(A16, A16, A16, A16, A16B, 2, 256, 128, 130, A16, 0, 0, None) == SHAPE    # K % 4
+    assert gw(A16, A16, A16, ODD, A16B, 2, 256, 128, 128, A16, 0, 0, None) == MISALIGNED
     assert L.fg_last_hip_error() == 0
 
 

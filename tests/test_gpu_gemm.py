@@ -296,3 +296,119 @@ def test_grouped_moe_down_projection_sampled():
     T = int(d["offsets"][-1])
     pts = sample_points(T, wl.MOE_HIDDEN, 2000, seed=15)
     _grouped_case(d["h"], d["w_down"], d["offsets"], bf16=True, pts=pts)
+
+
+# ------------------------------------------------------------------------------------------------
+# MoE backward: grouped Dgrad and grouped Wgrad, checked per expert against the oracle's Dgrad/Wgrad of
+# that expert's slice
+# ------------------------------------------------------------------------------------------------
+
+def _grouped_dgrad_case(dy, w, offsets, bf16=False, pts_per_group=None, pow2=False):
+    dyq, sdy = fg.fg_quantize_act_1x128(to_dev(dy), pow2=pow2)
+    G, N, K = w.shape
+    wq = torch.empty((G, N, K), dtype=torch.uint8, device=device())
+    sw = torch.empty((G, N // 128, (K + 127) // 128), dtype=torch.float32, device=device())
+    wd = to_dev(w)
+    for g in range(G):
+        fg.fg_quantize_w_128x128(wd[g], q=wq[g], scales=sw[g], pow2=pow2)
+    off = torch.from_numpy(np.asarray(offsets, np.int32)).to(device())
+    dx = fg.fg_fp8_grouped_gemm_dgrad(dyq, sdy, wq, sw, off, out_dtype=torch.bfloat16 if bf16 else torch.float32,
+                                      pow2=pow2)
+    torch.cuda.synchronize()
+    dyq_o, sdy_o = oracle.quantize_act_1x128(bits(dy), 0, pow2)
+    assert np.array_equal(np_u8(dyq), dyq_o)
+    out = _out_np(dx, bf16)
+    errs = []
+    for g in range(G):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 == r0:
+            continue
+        wq_o, sw_o = oracle.quantize_w_128x128(bits(w[g]), pow2)
+        pts = None if pts_per_group is None else sample_points(r1 - r0, K, pts_per_group, seed=31 + g)
+        prom, _ = oracle.gemm_dgrad(dyq_o[r0:r1], np.ascontiguousarray(sdy_o[:, r0:r1]), wq_o, sw_o, out_bf16=bf16,
+                                    pts=pts)
+        yo = out[r0:r1].reshape(-1)
+        yo = yo if pts is None else yo[pts]
+        errs.append(_cmp(yo, prom, bf16))
+    return errs
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_grouped_dgrad_small_with_empty_groups(bf16, pow2, tile):
+    device()
+    rng = np.random.default_rng(22)
+    offsets = [0, 0, 300, 301, 301, 700, 957]
+    T, N, K = offsets[-1], 256, 384
+    dy = _rand_act(rng, T, N, 1e-3)
+    w = wl.normal_bf16(rng, (len(offsets) - 1, N, K), 0.02)
+    _grouped_dgrad_case(dy, w, offsets, bf16, pow2=pow2)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_dgrad_moe_share_sampled(pow2):
+    device()
+    d = wl.moe_backward_inputs()
+    _grouped_dgrad_case(d["dy"], d["w_up"], d["offsets"], pts_per_group=300, pow2=pow2)
+
+
+def _grouped_wgrad_case(dy, x, offsets, init=None, pts_per_group=None, pow2=False):
+    dytq, sdyt = fg.fg_quantize_act_1x128(to_dev(dy), axis=fg.FG_ALONG_ROWS, pow2=pow2)
+    xtq, sxt = fg.fg_quantize_act_1x128(to_dev(x), axis=fg.FG_ALONG_ROWS, pow2=pow2)
+    T, N = dy.shape
+    K = x.shape[1]
+    G = len(offsets) - 1
+    off = torch.from_numpy(np.asarray(offsets, np.int32)).to(device())
+    if init is not None:
+        dw = fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, off, dw=to_dev(torch.from_numpy(init)), accumulate=True,
+                                          pow2=pow2)
+    else:
+        dw = fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, off, pow2=pow2)
+    torch.cuda.synchronize()
+    dytq_o, sdyt_o = oracle.quantize_act_1x128(bits(dy), 1, pow2)
+    xtq_o, sxt_o = oracle.quantize_act_1x128(bits(x), 1, pow2)
+    assert np.array_equal(np_u8(dytq), dytq_o) and np.array_equal(np_u8(xtq), xtq_o)
+    out = dw.cpu().numpy()
+    errs = []
+    for g in range(G):
+        t0, t1 = int(offsets[g]), int(offsets[g + 1])
+        pts = None if pts_per_group is None else sample_points(N, K, pts_per_group, seed=41 + g)
+        init_g = None if init is None else (init[g].reshape(-1) if pts is None else init[g].reshape(-1)[pts])
+        prom, _ = oracle.gemm_wgrad(np.ascontiguousarray(dytq_o[:, t0:t1]), np.ascontiguousarray(sdyt_o[t0 // 128: t1 // 128]),
+                                    np.ascontiguousarray(xtq_o[:, t0:t1]), np.ascontiguousarray(sxt_o[t0 // 128: t1 // 128]),
+                                    dw_init=init_g, pts=pts)
+        yo = out[g].reshape(-1)
+        yo = yo if pts is None else yo[pts]
+        if t1 == t0 and init is None:
+            assert not np.any(yo), "empty group must write zeros"
+            continue
+        errs.append(_cmp(yo, prom, False))
+    return errs
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_grouped_wgrad_small_with_empty_group(pow2, tile):
+    device()
+    rng = np.random.default_rng(23)
+    offsets = [0, 128, 128, 512, 640]                    # an empty group
+    T, N, K = offsets[-1], 200, 136
+    _grouped_wgrad_case(_rand_act(rng, T, N, 1e-3), _rand_act(rng, T, K), offsets, pow2=pow2)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_wgrad_accumulate(pow2):
+    device()
+    rng = np.random.default_rng(24)
+    offsets = [0, 256, 256, 384]
+    T, N, K = offsets[-1], 256, 264
+    init = (rng.standard_normal((3, N, K)) * 1e-3).astype(np.float32)
+    _grouped_wgrad_case(_rand_act(rng, T, N, 1e-3), _rand_act(rng, T, K), offsets, init=init, pow2=pow2)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_wgrad_moe_share_sampled(pow2):
+    device()
+    d = wl.moe_backward_inputs()
+    _grouped_wgrad_case(d["dy"], d["x"], d["offsets"], pts_per_group=300, pow2=pow2)
