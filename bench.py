@@ -63,6 +63,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-vendor", action="store_true")
+    ap.add_argument("--no-fused-epilogue", action="store_true")
     ap.add_argument("--pow2", action="store_true", help="power-of-2 scales (quantizers round scales up to 2^k; "
                     "the GEMMs then apply them in the matrix core)")
     ap.add_argument("--calib-copy", action="store_true", help="only run a 512 MiB device copy (counter calibration)")
@@ -242,6 +243,29 @@ def main():
         del scrub
         print("[bench] cold-cache quantize timings done", file=sys.stderr, flush=True)
 
+    # Fprop whose BF16 output is wanted as 1x128 FP8 tiles (the next layer's input): the GEMM writing BF16
+    # and a quantizer reading it back, against the GEMM quantizing in its epilogue (same codes and scales).
+    fused_epi = None
+    if not args.no_fused_epilogue:
+        ops[0][1]()
+        ops[1][1]()                             # X and W codes of the headline scale mode
+        yq = torch.empty((M, N), dtype=u8, device=dev)
+        sy = torch.empty((N // 128, M), dtype=f32, device=dev)
+        two = [("fprop_bf16", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=POW2),
+                "mfma", 2.0 * M * N * K),
+               ("quant_y_rowwise", lambda: fg.fg_quantize_act_1x128(B["y"], q=yq, scales=sy, pow2=POW2),
+                "hbm", quant_bytes(M, N))]
+        one = [("fprop_quant", lambda: fg.fg_fp8_gemm_fprop_quant(B["xq"], B["sx"], B["wq"], B["sw"], yq=yq, sy=sy,
+                                                                 pow2=POW2, out_pow2=POW2),
+                "mfma", 2.0 * M * N * K)]
+        ms2, per2 = measure(two, args.steps, args.warmup, "Fprop then quantize its output")
+        ms1, per1 = measure(one, args.steps, args.warmup, "Fprop quantizing in its epilogue")
+        fused_epi = {"separate_ms": round(ms2, 4), "separate_kernel_ms": {k: round(v, 4) for k, v in per2.items()},
+                     "fused_ms": round(ms1, 4), "fused_kernel_ms": round(per1["fprop_quant"], 4),
+                     "fused_TFLOP/s": round(2.0 * M * N * K / (per1["fprop_quant"] * 1e-3) / 1e12, 1),
+                     "speedup": round(ms2 / ms1, 3)}
+        del yq, sy
+
     # Grouped MoE GEMM (one GPU's expert share): up-projection then down-projection, BF16 out.
     moe = None
     if not args.no_moe:
@@ -371,6 +395,7 @@ def main():
         "quantize_cold_cache": cold,
         "vendor_fp8_gemm_reference": vendor,
         "moe_grouped": moe,
+        "fprop_output_quantized": fused_epi,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out))

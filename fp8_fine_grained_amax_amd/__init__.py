@@ -36,6 +36,7 @@ def lib():
         L.fg_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P, P]
         L.fg_quantize_act_1x128_both.argtypes = [P, I64, I64, I64, I, P, P, P, P, P]
         L.fg_fp8_gemm_fprop.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
+        L.fg_fp8_gemm_fprop_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, I, P]
         L.fg_fp8_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_gemm_wgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
@@ -160,6 +161,21 @@ def fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16, y=None, pow2: bo
     _check(lib().fg_fp8_gemm_fprop(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(y), _out_code(y.dtype),
                                    _mode(pow2), _stream(xq.device)), "fg_fp8_gemm_fprop")
     return y
+
+
+def fg_fp8_gemm_fprop_quant(xq, sx, wq, sw, yq=None, sy=None, pow2: bool = False, out_pow2: bool = False):
+    """Fprop whose BF16 output leaves the GEMM already quantized 1x128 along its columns: returns
+    (yq u8 [M, N], sy f32 [N/128, M]), equal to fg_quantize_act_1x128 of fg_fp8_gemm_fprop's BF16 Y."""
+    _gpu(xq, sx, wq, sw, yq, sy)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if yq is None:
+        yq = torch.empty((M, N), dtype=torch.uint8, device=xq.device)
+    if sy is None:
+        sy = torch.empty((N // 128, M), dtype=torch.float32, device=xq.device)
+    _check(lib().fg_fp8_gemm_fprop_quant(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(yq), _ptr(sy),
+                                         _mode(pow2), _mode(out_pow2), _stream(xq.device)), "fg_fp8_gemm_fprop_quant")
+    return yq, sy
 
 
 def fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.float32, dx=None, pow2: bool = False):

@@ -21,6 +21,9 @@ hipError_t fg_launch_quant_act_both(const uint16_t* x, int64_t rows, int64_t col
                                     uint8_t* qc, float* sc, uint8_t* qr, float* sr, hipStream_t stream);
 hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
                                 int64_t N, int64_t K, void* y, int out_bf16, int pow2, hipStream_t stream);
+hipError_t fg_launch_gemm_fprop_quant(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                      int64_t M, int64_t N, int64_t K, uint8_t* yq, float* sy, int pow2, int out_pow2,
+                                      hipStream_t stream);
 hipError_t fg_launch_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,
                                 int64_t N, int64_t K, void* dx, int out_bf16, int pow2, hipStream_t stream);
 hipError_t fg_launch_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
@@ -123,6 +126,19 @@ fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* w
     if (K % 128 != 0 || tiles(M, N) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw)) return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_fprop(xq, sx, wq, sw, M, N, K, y, out == FG_OUT_BF16, scales == FG_SCALE_POW2, stream));
+}
+
+fg_status fg_fp8_gemm_fprop_quant(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                                  int64_t N, int64_t K, uint8_t* yq, float* sy, fg_scale_mode scales,
+                                  fg_scale_mode out_scales, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || !valid_mode(scales) || !valid_mode(out_scales)) return FG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return FG_OK;
+    if (!yq || !sy || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
+    if (N % 128 != 0 || K % 128 != 0 || tiles(M, N) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(yq) || !aligned4(sx) || !aligned4(sw) || !aligned4(sy))
+        return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_gemm_fprop_quant(xq, sx, wq, sw, M, N, K, yq, sy, scales == FG_SCALE_POW2,
+                                               out_scales == FG_SCALE_POW2, stream));
 }
 
 fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw, int64_t M,

@@ -72,6 +72,7 @@ using Cfg8 = TileCfg<2, 4, 128, 64>;   // 256 x 256
 
 enum { SB_BLOCK = 0, SB_BLOCK_T = 1, SB_ROW = 2 };
 enum { GRP_NONE = 0, GRP_ROWS = 1, GRP_K = 2 };
+enum { EPI_STORE = 0, EPI_QUANT = 1 };
 
 struct GemmParams {
     const uint8_t* a;       // A-role codes [rows][K], row stride K
@@ -88,6 +89,9 @@ struct GemmParams {
     int64_t b_group_stride; // elements between consecutive groups' B
     int64_t sb_group_stride;
     int64_t out_group_stride; // GRP_K: elements between consecutive groups' outputs
+    uint8_t* q_out;           // EPI_QUANT: E4M3 codes of the BF16 output [M][N]
+    float* s_out;             // EPI_QUANT: their 1x128 scales [N/128][M]
+    int q_pow2;               // EPI_QUANT: power-of-2 output scales
 };
 
 // LDS swizzles. gfx950 serves a ds_read_b128 16 lanes (256 B, all 64 banks) at a time, and the 8 rows
@@ -121,7 +125,7 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* tile16, int lo_off, int hi
 // E8M0 code of an fp32 power of two in [2^-127, 2^127]: its biased exponent field.
 __device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23) & 0xFF; }
 
-template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2>
+template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE>
 __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     constexpr int BM = C::BM, BN = C::BN, NW = C::NW, MSUB = C::MSUB, NSUB = C::NSUB;
     constexpr int WAVE_M = C::WAVE_M, WAVE_N = C::WAVE_N;
@@ -514,6 +518,67 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
 
     __builtin_amdgcn_s_waitcnt(0);          // the last step's (redundant) staging loads
     // ---------------- epilogue ----------------
+    if constexpr (EPI == EPI_QUANT) {
+        // The BF16 output, quantized 1x128 along its columns exactly as fg_quantize_act_1x128 would quantize
+        // it (same max-abs, scale and quotient), without writing or re-reading the BF16 values. A 128-column
+        // group is two neighbouring 64-column wave tiles: each wave reduces its half of every row over the 4
+        // lanes holding it, and the pair exchange halves through LDS (the stages are idle by now).
+        static_assert(WAVE_N == 64 && BN % 128 == 0, "a 128-column group is a pair of 64-column wave tiles");
+        __syncthreads();                         // every wave's staging loads and LDS reads are done
+        uint32_t* rmax = reinterpret_cast<uint32_t*>(smem);   // [WAVES_N][BM] max |bf16| bits per row half
+        uint2 hb[MSUB][NSUB];                    // the lane's 4 BF16 values of each 16x16 tile, packed
+#pragma unroll
+        for (int i = 0; i < MSUB; i++) {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int j = 0; j < NSUB; j++) {
+                hb[i][j].x = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
+                hb[i][j].y = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
+                mx = fg_pk_max_u16(mx, fg_pk_max_u16(hb[i][j].x & 0x7FFF7FFFu, hb[i][j].y & 0x7FFF7FFFu));
+            }
+            mx = fg_max_halves(mx);
+            uint32_t o = (uint32_t)__shfl_xor((int)mx, 16);  // the 4 lanes holding a row: lane + 16 k
+            mx = o > mx ? o : mx;
+            o = (uint32_t)__shfl_xor((int)mx, 32);
+            mx = o > mx ? o : mx;
+            if (lane < 16) rmax[wn * BM + wm * WAVE_M + i * 16 + lrow] = mx;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MSUB; i++) {
+            const int row = wm * WAVE_M + i * 16 + lrow;
+            const uint32_t a0 = rmax[wn * BM + row], a1 = rmax[(wn ^ 1) * BM + row];
+            const float sc = fg_scale_from_amax_bits(a0 > a1 ? a0 : a1, p.q_pow2);
+            fg_divisor d = fg_make_divisor(sc, p.q_pow2);
+            // the quotient form, as in the standalone quantizer: exact product for pow2 scales, else the
+            // corrected quotient, moved up by 2^64 for the rows whose scale is below 2^-100
+            const int mode = p.q_pow2 ? FG_Q_POW2
+                           : (__builtin_amdgcn_ballot_w64(fg_divisor_tiny(d)) != 0 && fg_divisor_tiny(d)) ? FG_Q_TINY
+                                                                                                       : FG_Q_FAST;
+            if (mode == FG_Q_TINY) d = fg_divisor_shifted(d);
+            const int64_t m = m0 + row;
+            const bool row_ok = m < m_end;
+#pragma unroll
+            for (int j = 0; j < NSUB; j++) {
+                const uint32_t lo = hb[i][j].x, hi = hb[i][j].y;
+                uint32_t c;
+                if (mode == FG_Q_POW2) {
+                    c = fg_cvt2q<FG_Q_POW2, false>(fg_bf16_lo(lo), fg_bf16_hi(lo), d, 0);
+                    c = fg_cvt2q<FG_Q_POW2, true>(fg_bf16_lo(hi), fg_bf16_hi(hi), d, c);
+                } else if (mode == FG_Q_FAST) {
+                    c = fg_cvt2q<FG_Q_FAST, false>(fg_bf16_lo(lo), fg_bf16_hi(lo), d, 0);
+                    c = fg_cvt2q<FG_Q_FAST, true>(fg_bf16_lo(hi), fg_bf16_hi(hi), d, c);
+                } else {
+                    c = fg_cvt2q<FG_Q_TINY, false>(fg_bf16_lo(lo), fg_bf16_hi(lo), d, 0);
+                    c = fg_cvt2q<FG_Q_TINY, true>(fg_bf16_lo(hi), fg_bf16_hi(hi), d, c);
+                }
+                const int64_t n = wave_n0 + j * 16 + lcol4;
+                if (row_ok && n < N) *reinterpret_cast<uint32_t*>(p.q_out + m * N + n) = c;
+            }
+            if ((wn & 1) == 0 && lane < 16 && row_ok && wave_n0 < N) p.s_out[(wave_n0 >> 7) * p.M + m] = sc;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MSUB; i++) {
         const int64_t m = m0 + wm * WAVE_M + i * 16 + lrow;
@@ -547,9 +612,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     }
 }
 
-template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2>
+template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE>
 hipError_t launch_one(const GemmParams& p, unsigned grid, hipStream_t stream) {
-    auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUP, POW2>;
+    auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUP, POW2, EPI>;
     static bool attr_set = false;   // benign race: setting the attribute twice is harmless
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -667,4 +732,16 @@ hipError_t fg_launch_gemm_grouped_wgrad(const uint8_t* dytq, const float* sdyt, 
     p.offsets = offsets; p.G = G;
     p.out_group_stride = N * K;
     return launch<false, SB_ROW, GRP_K>(p, pow2, stream);
+}
+
+hipError_t fg_launch_gemm_fprop_quant(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                                      int64_t N, int64_t K, uint8_t* yq, float* sy, int pow2, int out_pow2,
+                                      hipStream_t stream) {
+    GemmParams p{};
+    p.a = xq; p.sa = sx; p.sa_ld = M; p.b = wq; p.sb = sw;
+    p.M = M; p.N = N; p.K = K; p.out = nullptr; p.out_bf16 = 1;
+    p.q_out = yq; p.s_out = sy; p.q_pow2 = out_pow2;
+    const unsigned grid = grid_for<Cfg8>(p, GRP_NONE);
+    return pow2 ? launch_one<Cfg8, false, SB_BLOCK, GRP_NONE, true, EPI_QUANT>(p, grid, stream)
+                : launch_one<Cfg8, false, SB_BLOCK, GRP_NONE, false, EPI_QUANT>(p, grid, stream);
 }

@@ -129,6 +129,20 @@ fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* w
                             int64_t M, int64_t N, int64_t K, void* y, fg_out_dtype out,
                             fg_scale_mode scales, hipStream_t stream);
 
+/* Fprop with the output quantized on chip: the BF16 Y of fg_fp8_gemm_fprop, quantized 1x128 along its
+ * columns (per token per 128 output channels, as the next layer's Fprop input needs it) before it leaves
+ * the GEMM. [W5], the passage of chip-design suggestions, describes the round trip this removes: BF16
+ * activations written to HBM, read back for quantization, FP8 codes written and read again for the next
+ * MMA. Here only the codes and scales reach HBM.
+ *   xq, sx, wq, sw as for fg_fp8_gemm_fprop (scales: their scale mode).
+ *   yq u8 [M][N], sy f32 [N/128][M]: bit-identical to fg_quantize_act_1x128(Y_bf16, FG_ALONG_COLS,
+ *   out_scales) applied to the BF16 output of fg_fp8_gemm_fprop on the same operands.
+ *   N % 128 == 0, K % 128 == 0, any M (M == 0 or N == 0: no-op; K == 0 quantizes zeros: codes 0,
+ *   scales 1). xq, wq, yq 16-byte aligned; scales 4-byte aligned. Always the 256x256 output tile. */
+fg_status fg_fp8_gemm_fprop_quant(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                  int64_t M, int64_t N, int64_t K, uint8_t* yq, float* sy,
+                                  fg_scale_mode scales, fg_scale_mode out_scales, hipStream_t stream);
+
 /* Dgrad (Figure 6, activation backward pass): dX[M][K] = dY[M][N] . W[N][K], contracting over N.
  *   dyq u8 [M][N], sdy f32 [N/128][M]   (dY quantized FG_ALONG_COLS)
  *   wq  u8 [N][K], sw f32 [N/128][K/128] (the same codes and 128x128 block scales as Fprop; the block

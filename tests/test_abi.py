@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -87,6 +87,13 @@ def test_gemm_rejections(L):
     assert f(A16, A16, None, A16, 128, 128, 128, A16, 0, 0, None) == INVALID  # null W
     assert f(A16, A16, A16, A16, 128, 128, 128, ODD, 0, 0, None) == MISALIGNED
     assert f(None, None, None, None, 0, 128, 128, None, 0, 0, None) == OK     # empty
+    fq = L.fg_fp8_gemm_fprop_quant
+    assert fq(A16, A16, A16, A16, 128, 200, 128, A16, A16, 0, 0, None) == SHAPE   # N % 128 (output groups)
+    assert fq(A16, A16, A16, A16, 128, 128, 100, A16, A16, 0, 0, None) == SHAPE   # K % 128
+    assert fq(A16, A16, A16, A16, 128, 128, 128, A16, A16, 0, 2, None) == INVALID # bad output scale mode
+    assert fq(A16, A16, A16, A16, 128, 128, 128, A16, None, 0, 0, None) == INVALID  # null output scales
+    assert fq(A16, A16, A16, A16, 128, 128, 128, ODD, A16, 0, 0, None) == MISALIGNED
+    assert fq(None, None, None, None, 0, 128, 128, None, None, 0, 0, None) == OK  # empty
     d = L.fg_fp8_gemm_dgrad
     assert d(A16, A16, A16, A16, 128, 200, 128, A16, 0, 0, None) == SHAPE     # N (contraction) % 128
     assert d(A16, A16, A16, A16, 128, 256, 200, A16, 0, 0, None) == SHAPE     # K % 128
