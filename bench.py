@@ -2,19 +2,24 @@
 
 One step = the whole hot path over one batch of the DeepSeek-V3-like dense MLP Linear
 (X [4096, 7168], W [18432, 7168], dY [4096, 18432], seeded synthetic bf16):
-  forward : quantize X (1x128 along channels), quantize W (128x128 blocks), Fprop  Y = X W^T (BF16 out)
-  backward: quantize dY (1x128 along channels), Dgrad dX = dY W (FP32 out),
-            quantize dY and X (1x128 along tokens, transposed), Wgrad dW = dY^T X (FP32 out)
+  forward : quantize X in both 1x128 tilings (along channels for Fprop, along tokens for Wgrad, one read),
+            quantize W (128x128 blocks), Fprop Y = X W^T (BF16 out)
+  backward: quantize dY in both tilings (one read), Dgrad dX = dY W (FP32 out), Wgrad dW = dY^T X (FP32 out)
 `value` is the FP8 GEMM throughput of the whole step (3 x 2MNK FLOP over the step's wall time), with
 all inputs resident in HBM when the timed region starts. Per-kernel times come from HIP events on the
-stream the kernels run on. Also reported: per-kernel roofline fractions, cold-cache quantize bandwidth
-(a 1 GiB read between launches defeats the 256 MB Infinity Cache), the grouped MoE GEMM on one GPU's
-expert share, and the CPU oracle timed on a bounded sample of the same workload.
+stream the kernels run on.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pow2] [--no-moe] [--no-cpu] [--no-cold] [--calib-copy]
+Also reported, beside the headline: the same step with the other scale mode and with one quantizer
+launch per tiling ("variants"), per-kernel roofline fractions, cold-cache quantize bandwidth (a 1 GiB
+read between launches defeats the 256 MB Infinity Cache), the Fprop that quantizes its own output
+against Fprop + quantizer, per-tensor (current and delayed) scaling against the 1x128 tiles, the grouped
+MoE GEMMs on one GPU's expert share, the vendor's per-tensor FP8 GEMM at the Fprop shape, and the CPU
+oracle timed on a bounded sample of the workload.
 
-The headline uses fp32 scales (amax/448); --pow2 makes power-of-2 scales the headline. The other mode is
-always measured too, on the same inputs, and reported under "other_scale_mode".
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pow2] [--no-moe] [--no-cpu] [--no-cold]
+       [--no-vendor] [--no-fused-epilogue] [--no-per-tensor] [--calib-copy]
+
+The headline uses fp32 scales (amax/448); --pow2 makes power-of-2 scales the headline.
 """
 import argparse
 import hashlib
@@ -64,6 +69,7 @@ def main():
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-vendor", action="store_true")
     ap.add_argument("--no-fused-epilogue", action="store_true")
+    ap.add_argument("--no-per-tensor", action="store_true")
     ap.add_argument("--pow2", action="store_true", help="power-of-2 scales (quantizers round scales up to 2^k; "
                     "the GEMMs then apply them in the matrix core)")
     ap.add_argument("--calib-copy", action="store_true", help="only run a 512 MiB device copy (counter calibration)")
@@ -266,6 +272,30 @@ def main():
                      "speedup": round(ms2 / ms1, 3)}
         del yq, sy
 
+    # Contrast baseline: per-tensor scaling of X and dY. Current scaling needs the tensor's max-abs first
+    # (a second read of the input); delayed scaling takes it from a history and records the new one in
+    # the same pass. Timed beside the 1x128 quantizer of the same tensor.
+    per_tensor = None
+    if not args.no_per_tensor:
+        per_tensor = {}
+        hist = torch.zeros((16,), dtype=f32, device=dev)
+        hist[0] = 1.0
+        for tname, t, (rows, cols), qb, sb in (("x", x, (M, K), B["xq"], B["sx"]), ("dy", dy, (M, N), B["dyq"], B["sdy"])):
+            cur = torch.zeros((1,), dtype=f32, device=dev)
+            rec = torch.zeros((1,), dtype=f32, device=dev)
+            seq = [("amax", lambda: (cur.zero_(), fg.fg_amax_bf16(t, amax=cur)), "hbm", rows * cols * 2),
+                   ("quant_current", lambda: fg.fg_quantize_per_tensor(t, cur, q=qb, scales=sb), "hbm",
+                    quant_bytes(rows, cols))]
+            dl = [("quant_delayed", lambda: (rec.zero_(), fg.fg_quantize_per_tensor(t, hist, q=qb, scales=sb, amax_out=rec)), "hbm",
+                   quant_bytes(rows, cols))]
+            tl = [("quant_1x128", lambda: fg.fg_quantize_act_1x128(t, q=qb, scales=sb), "hbm", quant_bytes(rows, cols))]
+            ms_c, per_c = measure(seq, args.steps, args.warmup, f"per-tensor current scaling of {tname}")
+            ms_d, _ = measure(dl, args.steps, args.warmup, f"per-tensor delayed scaling of {tname}")
+            ms_t, _ = measure(tl, args.steps, args.warmup, f"1x128 quantization of {tname}")
+            per_tensor[tname] = {"shape": [rows, cols], "current_ms": round(ms_c, 4),
+                                 "current_kernel_ms": {k: round(v, 4) for k, v in per_c.items()},
+                                 "delayed_ms": round(ms_d, 4), "tiles_1x128_ms": round(ms_t, 4)}
+
     # Grouped MoE GEMM (one GPU's expert share): up-projection then down-projection, BF16 out.
     moe = None
     if not args.no_moe:
@@ -396,6 +426,7 @@ def main():
         "vendor_fp8_gemm_reference": vendor,
         "moe_grouped": moe,
         "fprop_output_quantized": fused_epi,
+        "per_tensor_contrast": per_tensor,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out))

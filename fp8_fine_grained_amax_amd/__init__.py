@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8fg.so")
 FG_SCALE_FP32, FG_SCALE_POW2 = 0, 1
 FG_OUT_F32, FG_OUT_BF16 = 0, 1
 FG_ALONG_COLS, FG_ALONG_ROWS = 0, 1
+FG_LAYOUT_ACT_1x128, FG_LAYOUT_W_128x128 = 0, 1
 
 _lib = None
 
@@ -42,8 +43,11 @@ def lib():
         L.fg_fp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
-        for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop", "fg_fp8_gemm_dgrad",
-                  "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm", "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad"):
+        L.fg_amax_bf16.argtypes = [P, I64, I64, I64, P, P]
+        L.fg_quantize_per_tensor.argtypes = [P, I64, I64, I64, P, I64, I, I, P, P, P, P]
+        for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop",
+                  "fg_fp8_gemm_fprop_quant", "fg_fp8_gemm_dgrad", "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm",
+                  "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad", "fg_amax_bf16", "fg_quantize_per_tensor"):
             getattr(L, f).restype = I
         L.fg_status_string.argtypes = [I]
         L.fg_status_string.restype = ctypes.c_char_p
@@ -144,6 +148,43 @@ def fg_quantize_w_128x128(w, pow2: bool = False, q=None, scales=None):
         scales = torch.empty(((n + 127) // 128, (k + 127) // 128), dtype=torch.float32, device=w.device)
     _check(lib().fg_quantize_w_128x128(_ptr(w), n, k, w.stride(0), FG_SCALE_POW2 if pow2 else FG_SCALE_FP32,
                                        _ptr(q), _ptr(scales), _stream(w.device)), "fg_quantize_w_128x128")
+    return q, scales
+
+
+def _bf16_2d(x, what):
+    _gpu(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise Fp8fgError(f"{what} must be a 2-D bf16 tensor with unit column stride")
+    return x.shape
+
+
+def fg_amax_bf16(x, amax=None):
+    """max |x| of a bf16 matrix, folded into the device float amax (a new zero-filled one if None)."""
+    rows, cols = _bf16_2d(x, "x")
+    if amax is None:
+        amax = torch.zeros((1,), dtype=torch.float32, device=x.device)
+    _gpu(amax)
+    _check(lib().fg_amax_bf16(_ptr(x), rows, cols, x.stride(0), _ptr(amax), _stream(x.device)), "fg_amax_bf16")
+    return amax
+
+
+def fg_quantize_per_tensor(x, amax_hist, pow2: bool = False, layout: int = FG_LAYOUT_ACT_1x128, q=None, scales=None,
+                           amax_out=None):
+    """One E4M3 scale for the whole bf16 matrix x [rows, cols] from the device max-abs history amax_hist
+    (1-D float32). Returns (q uint8 [rows, cols], scales) with scales broadcast in the 1x128 activation
+    layout [cols/128, rows] or the 128x128 weight layout [ceil(rows/128), cols/128]."""
+    rows, cols = _bf16_2d(x, "x")
+    _gpu(amax_hist, amax_out)
+    if amax_hist.dtype != torch.float32 or amax_hist.dim() != 1 or not amax_hist.is_contiguous():
+        raise Fp8fgError("amax_hist must be a contiguous 1-D float32 tensor")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        shape = (cols // 128, rows) if layout == FG_LAYOUT_ACT_1x128 else ((rows + 127) // 128, cols // 128)
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check(lib().fg_quantize_per_tensor(_ptr(x), rows, cols, x.stride(0), _ptr(amax_hist), amax_hist.numel(),
+                                        _mode(pow2), layout, _ptr(q), _ptr(scales), _ptr(amax_out),
+                                        _stream(x.device)), "fg_quantize_per_tensor")
     return q, scales
 
 

@@ -32,6 +32,11 @@ hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint
                                   const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, void* y,
                                   int out_bf16, int pow2, hipStream_t stream);
 
+hipError_t fg_launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax, hipStream_t stream);
+hipError_t fg_launch_quant_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* hist,
+                                      int64_t n_hist, int pow2, int64_t n_scales, uint8_t* q, float* scales,
+                                      float* amax_out, hipStream_t stream);
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -41,6 +46,7 @@ constexpr int64_t kMaxGridX = 2147483647LL;
 constexpr int64_t kMaxGridY = 65535LL;
 constexpr int64_t kMaxGemmTiles = 2147483647LL;
 constexpr int32_t kMaxGroups = 65536;
+constexpr int64_t kMaxFlatChunks = 1LL << 31;   // per-tensor kernels index 16 B chunks in 32 bits
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -59,6 +65,34 @@ int64_t tiles(int64_t a, int64_t b) { return ((a + 255) / 256) * ((b + 127) / 12
 }  // namespace
 
 extern "C" {
+
+fg_status fg_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || ld_x < cols) return FG_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return FG_OK;
+    if (!x || !amax) return FG_ERR_INVALID_ARG;
+    if (cols % 8 != 0 || rows * (cols / 8) >= kMaxFlatChunks) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(x) || !aligned4(amax) || (ld_x % 8) != 0) return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_amax((const uint16_t*)x, rows, cols, ld_x, amax, stream));
+}
+
+fg_status fg_quantize_per_tensor(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const float* amax_hist,
+                                 int64_t n_hist, fg_scale_mode mode, fg_scale_layout layout, uint8_t* q,
+                                 float* scales, float* amax_out, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || ld_x < cols || n_hist < 0 || !valid_mode(mode) ||
+        (layout != FG_LAYOUT_ACT_1x128 && layout != FG_LAYOUT_W_128x128))
+        return FG_ERR_INVALID_ARG;
+    if (rows == 0) return FG_OK;
+    if (!x || !q || !scales || (n_hist > 0 && !amax_hist)) return FG_ERR_INVALID_ARG;
+    if (amax_out && n_hist > 0 && amax_out >= amax_hist && amax_out < amax_hist + n_hist) return FG_ERR_INVALID_ARG;
+    if (cols % 128 != 0 || n_hist > 4096 || rows * (cols / 8) >= kMaxFlatChunks) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (cols == 0) return FG_OK;
+    if (!aligned16(x) || !aligned16(q) || (ld_x % 8) != 0 || !aligned4(scales) || (amax_hist && !aligned4(amax_hist)) ||
+        (amax_out && !aligned4(amax_out)))
+        return FG_ERR_MISALIGNED;
+    const int64_t n_scales = layout == FG_LAYOUT_ACT_1x128 ? (cols / 128) * rows : ((rows + 127) / 128) * (cols / 128);
+    return from_hip(fg_launch_quant_per_tensor((const uint16_t*)x, rows, cols, ld_x, amax_hist, n_hist,
+                                               mode == FG_SCALE_POW2, n_scales, q, scales, amax_out, stream));
+}
 
 const char* fg_status_string(fg_status s) {
     switch (s) {

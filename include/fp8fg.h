@@ -198,6 +198,45 @@ fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, cons
                                     const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
                                     float* dw, int accumulate, fg_scale_mode scales, hipStream_t stream);
 
+/* ---- Per-tensor scaling: the contrast baseline ----------------------------------------------------
+ * The usual FP8 recipe that the fine-grained tiles replace ([W1], the passage on aligning a whole
+ * tensor's max-abs to the largest FP8 value and on its sensitivity to activation outliers) and its
+ * delayed variant ([W4], the passage on delayed quantization, which infers the current max-abs from a
+ * history kept over earlier iterations). */
+
+/* Max-abs of a bf16 tensor.
+ *   x     bf16 [rows][cols], row stride ld_x; cols % 8 == 0, ld_x % 8 == 0, x 16-byte aligned;
+ *         rows * cols < 2^34.
+ *   amax  DEVICE float, 4-byte aligned: on completion *amax = max(*amax, max |x|). It is an atomic max on
+ *         the float's bits, so *amax must hold a non-negative float on entry (0 for the tensor's own
+ *         max-abs). The max-abs is exact (a bf16 value).
+ *   rows == 0 or cols == 0: no-op. */
+fg_status fg_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax, hipStream_t stream);
+
+typedef enum {
+    FG_LAYOUT_ACT_1x128 = 0,   /* f32 [cols/128][rows], as fg_quantize_act_1x128 along the columns */
+    FG_LAYOUT_W_128x128 = 1    /* f32 [ceil(rows/128)][cols/128], as fg_quantize_w_128x128         */
+} fg_scale_layout;
+
+/* One scale for the whole tensor, taken from a device-resident max-abs history:
+ *   A = max over i < n_hist of |amax_hist[i]|, rounded up to a bf16 value and capped at the largest
+ *       finite bf16 (A = 0 for n_hist == 0);
+ *   s = the scale rule of the 1x128 quantizers applied to A (A == 0 gives s = 1; mode as there);
+ *   q = E4M3 code of RN_f32(x / s); quotients beyond +-448 (values above A) saturate to +-448.
+ * n_hist == 1 holding the tensor's own max-abs (from fg_amax_bf16) is current per-tensor scaling, two
+ * reads of x. Earlier iterations' max-abs values are delayed scaling, one read.
+ *   x        bf16 [rows][cols], row stride ld_x; cols % 128 == 0; any rows; rows * cols < 2^34.
+ *   amax_hist DEVICE floats, finite; 0 <= n_hist <= 4096.
+ *   q        u8 [rows][cols] (row stride cols).
+ *   scales   every entry set to s, in `layout`, so the GEMMs of this header take q and scales unchanged.
+ *   amax_out NULL, or a DEVICE float outside amax_hist[0, n_hist): *amax_out = max(*amax_out, max |x|),
+ *            as fg_amax_bf16 (records this tensor's max-abs for the next iteration's history).
+ *   Alignment: x, q 16-byte aligned; ld_x % 8 == 0; scales, amax_hist, amax_out 4-byte aligned.
+ *   rows == 0: no-op. */
+fg_status fg_quantize_per_tensor(const void* x, int64_t rows, int64_t cols, int64_t ld_x, const float* amax_hist,
+                                 int64_t n_hist, fg_scale_mode mode, fg_scale_layout layout, uint8_t* q,
+                                 float* scales, float* amax_out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* fg_status_string(fg_status s);
 

@@ -34,6 +34,9 @@ def lib():
         L.oracle_scale_from_amax.argtypes = [ctypes.c_float, I]
         L.oracle_quantize_act_1x128.argtypes = [P, I64, I64, I64, I, I, P, P]
         L.oracle_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P]
+        L.oracle_amax_bf16.restype = ctypes.c_float
+        L.oracle_amax_bf16.argtypes = [P, I64, I64, I64]
+        L.oracle_quantize_per_tensor.argtypes = [P, I64, I64, I64, P, I64, I, I, P, P]
         L.oracle_gemm_fprop.argtypes = [P, P, P, P, I64, I64, I64, P, I64, I, P, P]
         L.oracle_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I64, I, P, P]
         L.oracle_gemm_wgrad.argtypes = [P, P, P, P, I64, I64, I64, I, P, I64, P, P]
@@ -96,6 +99,27 @@ def quantize_w_128x128(w_bits, pow2: bool):
     q = np.empty((n, k), np.uint8)
     s = np.empty(((n + 127) // 128, (k + 127) // 128), np.float32)
     lib().oracle_quantize_w_128x128(_p(w), n, k, k, int(pow2), _p(q), _p(s))
+    return q, s
+
+
+def amax_bf16(x_bits):
+    """max |x| of a uint16 bf16 matrix, as a float."""
+    x = _u16(x_bits)
+    rows, cols = x.shape
+    return float(lib().oracle_amax_bf16(_p(x), rows, cols, cols))
+
+
+def quantize_per_tensor(x_bits, hist, pow2: bool, layout: int = 0):
+    """One scale for the whole matrix from the max-abs history hist (floats). layout 0: scales broadcast
+    as [ceil(cols/128), rows]; layout 1: as [ceil(rows/128), ceil(cols/128)]. Returns (q, scales)."""
+    x = _u16(x_bits)
+    rows, cols = x.shape
+    h = np.ascontiguousarray(np.asarray(hist, np.float32).reshape(-1))
+    q = np.empty((rows, cols), np.uint8)
+    shape = ((cols + 127) // 128, rows) if layout == 0 else ((rows + 127) // 128, (cols + 127) // 128)
+    s = np.empty(shape, np.float32)
+    lib().oracle_quantize_per_tensor(_p(x), rows, cols, cols, _p(h) if h.size else None, h.size, int(pow2),
+                                     int(layout), _p(q), _p(s))
     return q, s
 
 

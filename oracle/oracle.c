@@ -184,6 +184,49 @@ void oracle_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t 
 }
 
 /* ------------------------------------------------------------------------------------------------ */
+/* Per-tensor scaling: the prior practice the tiles are contrasted with                             */
+/* ------------------------------------------------------------------------------------------------ */
+
+/* Max-abs of a whole bf16 tensor ([W1], the passage on aligning the input tensor's max-abs to the
+ * largest FP8 value, the common practice it calls sensitive to activation outliers). */
+float oracle_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld) {
+    return amax_of(x, rows, cols, ld);
+}
+
+/* The max-abs a per-tensor scale is taken from: the largest |h[i]| of a history ([W4], the passage on
+ * delayed quantization, which infers the current max-abs from those of prior iterations; one entry
+ * holding the tensor's own max-abs is current scaling). Readings: a value between two bf16 numbers is
+ * taken as the next bf16 number up, and values beyond the largest finite bf16 as that number. */
+static float hist_amax(const float* h, int64_t n) {
+    double m = 0.0;
+    for (int64_t i = 0; i < n; i++)
+        if (fabs((double)h[i]) > m) m = fabs((double)h[i]);
+    const double bf16_max = ldexp(255.0 / 128.0, 127);           /* (2 - 2^-7) * 2^127          */
+    if (m >= bf16_max) return (float)bf16_max;
+    if (m == 0.0) return 0.0f;
+    int e;
+    frexp(m, &e);                                                  /* m in [2^(e-1), 2^e)          */
+    double ulp = ldexp(1.0, (e - 1) - 7);                          /* bf16 spacing: 7 fraction bits */
+    if (e - 1 < -126) ulp = ldexp(1.0, -133);                      /* subnormal bf16 spacing        */
+    return (float)(ceil(m / ulp) * ulp);
+}
+
+/* Per-tensor quantization: s from the history's max-abs by the same rule as the tiles (R3, R4), codes
+ * enc(RN_f32(x / s)) with saturation above 448 (R2) for values beyond that max-abs. Every scale entry of
+ * the layout (0: the 1x128 activation layout [cols/128][rows]; 1: the 128x128 weight layout
+ * [ceil(rows/128)][cols/128]) holds s. */
+void oracle_quantize_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* hist,
+                                int64_t n_hist, int pow2, int layout, uint8_t* q, float* scales) {
+    float s = oracle_scale_from_amax(hist_amax(hist, n_hist), pow2);
+    int64_t n_scales = layout == 0 ? ((cols + GROUP - 1) / GROUP) * rows
+                                   : ((rows + GROUP - 1) / GROUP) * ((cols + GROUP - 1) / GROUP);
+    for (int64_t i = 0; i < n_scales; i++) scales[i] = s;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            q[r * cols + c] = oracle_e4m3_encode(oracle_bf16_to_f32(x[r * ld + c]) / s);
+}
+
+/* ------------------------------------------------------------------------------------------------ */
 /* Block-scaled GEMM                                                                                */
 /* ------------------------------------------------------------------------------------------------ */
 

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -122,3 +122,21 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(fg.Fp8fgError):
         fg.fg_quantize_act_1x128(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def test_per_tensor_rejections(L):
+    a = L.fg_amax_bf16
+    assert a(A16, 4, 124, 128, A16B, None) == SHAPE                  # cols % 8
+    assert a(A16, 4, 128, 100, A16B, None) == INVALID                # ld < cols
+    assert a(A16, 4, 128, 128, None, None) == INVALID                # null amax
+    assert a(ODD, 4, 128, 128, A16B, None) == MISALIGNED
+    assert a(None, 0, 128, 128, None, None) == OK                    # empty
+    q = L.fg_quantize_per_tensor
+    assert q(A16, 4, 100, 104, A16B, 1, 0, 0, A16, A16, None, None) == SHAPE       # cols % 128
+    assert q(A16, 4, 128, 128, A16B, 5000, 0, 0, A16, A16, None, None) == SHAPE    # history too long
+    assert q(A16, 4, 128, 128, A16B, 1, 3, 0, A16, A16, None, None) == INVALID     # bad mode
+    assert q(A16, 4, 128, 128, A16B, 1, 0, 2, A16, A16, None, None) == INVALID     # bad layout
+    assert q(A16, 4, 128, 128, None, 1, 0, 0, A16, A16, None, None) == INVALID     # null history
+    assert q(A16, 4, 128, 128, A16B, 4, 0, 0, A16, A16, A16B + 8, None) == INVALID  # amax_out inside history
+    assert q(A16, 4, 128, 128, A16B, 1, 0, 0, ODD, A16, None, None) == MISALIGNED
+    assert q(None, 0, 128, 128, None, 0, 0, 0, None, None, None, None) == OK       # empty
