@@ -296,6 +296,23 @@ def main():
                                  "current_kernel_ms": {k: round(v, 4) for k, v in per_c.items()},
                                  "delayed_ms": round(ms_d, 4), "tiles_1x128_ms": round(ms_t, 4)}
 
+    # Token tiles for Wgrad from activations cached as 1x128 FP8 tiles (read codes, dequantize, transpose,
+    # re-quantize) against quantizing the bf16 activations along the tokens directly.
+    requant = None
+    if not args.no_per_tensor:
+        requant = {}
+        for tname, t, (rows, cols), qb, sb, qtb, stb in (("x", x, (M, K), B["xq"], B["sx"], B["xtq"], B["sxt"]),
+                                                          ("dy", dy, (M, N), B["dyq"], B["sdy"], B["dytq"], B["sdyt"])):
+            fg.fg_quantize_act_1x128(t, q=qb, scales=sb, pow2=POW2)
+            rq = [("requant", lambda: fg.fg_requantize_1x128_to_tokens(qb, sb, pow2=POW2, q_out=qtb, s_out=stb), "hbm", 2 * rows * cols + 2 * rows * cols // 128 * 4)]
+            ms_r, _ = measure(rq, args.steps, args.warmup, f"re-quantization of cached {tname} into token tiles")
+            dr = [("direct", lambda: fg.fg_quantize_act_1x128(t, axis=fg.FG_ALONG_ROWS, q=qtb, scales=stb, pow2=POW2),
+                   "hbm", quant_bytes(rows, cols))]
+            ms_d, _ = measure(dr, args.steps, args.warmup, f"token tiles of {tname} from bf16")
+            gbps = (2 * rows * cols + 2 * rows * cols // 128 * 4) / (ms_r * 1e-3) / 1e9
+            requant[tname] = {"shape": [rows, cols], "requant_ms": round(ms_r, 4), "requant_GB/s": round(gbps, 1),
+                              "from_bf16_ms": round(ms_d, 4)}
+
     # Grouped MoE GEMM (one GPU's expert share): up-projection then down-projection, BF16 out.
     moe = None
     if not args.no_moe:
@@ -427,6 +444,7 @@ def main():
         "moe_grouped": moe,
         "fprop_output_quantized": fused_epi,
         "per_tensor_contrast": per_tensor,
+        "requantize_tokens": requant,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out))

@@ -44,10 +44,12 @@ def lib():
         L.fg_fp8_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_amax_bf16.argtypes = [P, I64, I64, I64, P, P]
+        L.fg_requantize_1x128_to_tokens.argtypes = [P, P, I64, I64, I, P, P, P]
         L.fg_quantize_per_tensor.argtypes = [P, I64, I64, I64, P, I64, I, I, P, P, P, P]
         for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop",
                   "fg_fp8_gemm_fprop_quant", "fg_fp8_gemm_dgrad", "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm",
-                  "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad", "fg_amax_bf16", "fg_quantize_per_tensor"):
+                  "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad", "fg_amax_bf16", "fg_quantize_per_tensor",
+                  "fg_requantize_1x128_to_tokens"):
             getattr(L, f).restype = I
         L.fg_status_string.argtypes = [I]
         L.fg_status_string.restype = ctypes.c_char_p
@@ -134,6 +136,20 @@ def fg_quantize_act_1x128_both(x, pow2: bool = False, q_cols=None, scales_cols=N
                                             _ptr(q_cols), _ptr(scales_cols), _ptr(q_rows), _ptr(scales_rows),
                                             _stream(dev)), "fg_quantize_act_1x128_both")
     return q_cols, scales_cols, q_rows, scales_rows
+
+
+def fg_requantize_1x128_to_tokens(q_in, s_in, pow2: bool = False, q_out=None, s_out=None):
+    """Token tiles from cached 1x128 FP8 tiles: q_in uint8 [rows, cols] and s_in f32 [cols/128, rows] (as
+    fg_quantize_act_1x128 along columns) -> (q_out uint8 [cols, rows], s_out f32 [rows/128, cols])."""
+    _gpu(q_in, s_in, q_out, s_out)
+    rows, cols = q_in.shape
+    if q_out is None:
+        q_out = torch.empty((cols, rows), dtype=torch.uint8, device=q_in.device)
+    if s_out is None:
+        s_out = torch.empty((rows // 128, cols), dtype=torch.float32, device=q_in.device)
+    _check(lib().fg_requantize_1x128_to_tokens(_ptr(q_in), _ptr(s_in), rows, cols, _mode(pow2), _ptr(q_out),
+                                               _ptr(s_out), _stream(q_in.device)), "fg_requantize_1x128_to_tokens")
+    return q_out, s_out
 
 
 def fg_quantize_w_128x128(w, pow2: bool = False, q=None, scales=None):

@@ -9,6 +9,8 @@ hipError_t fg_launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t col
                                     uint8_t* q, float* scales, hipStream_t stream);
 hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
                                     uint8_t* q, float* scales, hipStream_t stream);
+hipError_t fg_launch_requant_rows(const uint8_t* q_in, const float* s_in, int64_t rows, int64_t cols, int pow2,
+                                  uint8_t* q, float* scales, hipStream_t stream);
 hipError_t fg_launch_quant_w(const uint16_t* w, int64_t n, int64_t k, int64_t ld, int pow2, uint8_t* q,
                              float* scales, hipStream_t stream);
 hipError_t fg_launch_gemm_grouped_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
@@ -139,6 +141,17 @@ fg_status fg_quantize_act_1x128_both(const void* x, int64_t rows, int64_t cols, 
     if (cols / 128 > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_quant_act_both((const uint16_t*)x, rows, cols, ld_x, mode == FG_SCALE_POW2, q_cols,
                                              scales_cols, q_rows, scales_rows, stream));
+}
+
+fg_status fg_requantize_1x128_to_tokens(const uint8_t* q_in, const float* s_in, int64_t rows, int64_t cols,
+                                        fg_scale_mode mode, uint8_t* q_out, float* s_out, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || !valid_mode(mode)) return FG_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return FG_OK;
+    if (!q_in || !s_in || !q_out || !s_out) return FG_ERR_INVALID_ARG;
+    if (rows % 128 != 0 || cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(q_in) || !aligned16(s_in) || !aligned16(q_out) || !aligned4(s_out)) return FG_ERR_MISALIGNED;
+    if (cols / 64 > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    return from_hip(fg_launch_requant_rows(q_in, s_in, rows, cols, mode == FG_SCALE_POW2, q_out, s_out, stream));
 }
 
 fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_w, fg_scale_mode mode, uint8_t* q,

@@ -66,10 +66,31 @@ __global__ __launch_bounds__(256) void fg_quant_act_cols_kernel(const uint16_t* 
 // transpose buffer [64 cols][128 rows], and leave as 16 B stores: 128 contiguous bytes per column.
 // Workgroups are numbered row block first, so the ones in flight together extend the same output
 // columns: their 128 B pieces form contiguous runs of the transposed codes.
+//
+// FROM_CODES: the input is not bf16 but FP8 codes cached in 1x128 tiles along the columns (codes
+// [rows][cols], row scales [cols/128][rows]). Each element is dequantized to the bf16 activation it
+// stands for, bf16(RN_f32(code * row scale)), and that tensor is quantized along the tokens exactly as a
+// bf16 input would be: the read, dequantize, transpose and re-quantize step of the backward pass.
 // ------------------------------------------------------------------------------------------------
+// Eight E4M3 codes (8 B) times their row's scale, rounded to fp32 and then to bf16: eight bf16 values.
+__device__ __forceinline__ uint32_t fg_dequant2_bf16(float lo, float hi, float s) {
+    return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)(lo * s)) |
+           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)(hi * s)) << 16);
+}
+__device__ __forceinline__ uint4 fg_dequant8_bf16(uint2 c, float s) {
+    // exact E4M3 -> fp32 decode of bytes 0-1 (false) or 2-3 (true) of a dword
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+    const auto e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false), f = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+    return make_uint4(fg_dequant2_bf16(a[0], a[1], s), fg_dequant2_bf16(b[0], b[1], s),
+                      fg_dequant2_bf16(e[0], e[1], s), fg_dequant2_bf16(f[0], f[1], s));
+}
+
+template <bool FROM_CODES>
 __global__ __launch_bounds__(256) void fg_quant_act_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                 int64_t cols, int64_t ld, int pow2,
-                                                                uint8_t* __restrict__ q, float* __restrict__ scales) {
+                                                                uint8_t* __restrict__ q, float* __restrict__ scales,
+                                                                const uint8_t* __restrict__ q_in,
+                                                                const float* __restrict__ s_in) {
     __shared__ uint32_t colmax[4][32];          // [wave][column pair], packed u16 max-abs
     __shared__ float col_s[64], col_r[64];      // per-column scale and reciprocal
     __shared__ int any_tiny;
@@ -84,12 +105,24 @@ __global__ __launch_bounds__(256) void fg_quant_act_rows_kernel(const uint16_t* 
     const bool col_ok = col < cols;
 
     uint4 v[4];
+    if constexpr (FROM_CODES) {
+        // the 64-column tile lies inside one 128-column group: one row scale per row
+        const float4 sr = col_ok ? *reinterpret_cast<const float4*>(s_in + (col / FG_GROUP) * rows + r0 + 4 * rgrp)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        if (col_ok)
-            v[i] = *reinterpret_cast<const uint4*>(x + (r0 + 4 * rgrp + i) * ld + col);
-        else
-            v[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < 4; i++) {
+            const uint2 c = col_ok ? *reinterpret_cast<const uint2*>(q_in + (r0 + 4 * rgrp + i) * cols + col)
+                                   : make_uint2(0, 0);
+            v[i] = fg_dequant8_bf16(c, (&sr.x)[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if (col_ok)
+                v[i] = *reinterpret_cast<const uint4*>(x + (r0 + 4 * rgrp + i) * ld + col);
+            else
+                v[i] = make_uint4(0, 0, 0, 0);
+        }
     }
     // packed max-abs per column pair over this thread's 4 rows
     uint32_t m[4];
@@ -345,7 +378,16 @@ hipError_t fg_launch_quant_act_cols(const uint16_t* x, int64_t rows, int64_t col
 hipError_t fg_launch_quant_act_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
                                     uint8_t* q, float* scales, hipStream_t stream) {
     dim3 grid((unsigned)(rows / FG_GROUP), (unsigned)((cols + 63) / 64));
-    hipLaunchKernelGGL(fg_quant_act_rows_kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, pow2, q, scales);
+    hipLaunchKernelGGL(fg_quant_act_rows_kernel<false>, grid, dim3(256), 0, stream, x, rows, cols, ld, pow2, q, scales,
+                       nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t fg_launch_requant_rows(const uint8_t* q_in, const float* s_in, int64_t rows, int64_t cols, int pow2,
+                                  uint8_t* q, float* scales, hipStream_t stream) {
+    dim3 grid((unsigned)(rows / FG_GROUP), (unsigned)(cols / 64));
+    hipLaunchKernelGGL(fg_quant_act_rows_kernel<true>, grid, dim3(256), 0, stream, nullptr, rows, cols, cols, pow2, q,
+                       scales, q_in, s_in);
     return hipGetLastError();
 }
 

@@ -111,6 +111,23 @@ fg_status fg_quantize_act_1x128_both(const void* x, int64_t rows, int64_t cols, 
                                      uint8_t* q_cols, float* scales_cols, uint8_t* q_rows, float* scales_rows,
                                      hipStream_t stream);
 
+/* Token tiles from cached FP8 activations. The activations Wgrad needs are kept in FP8 for the backward
+ * pass ([W4]/[W5], Figure 6 passage), as 1x128 tiles along the channels; Wgrad contracts over tokens and
+ * needs tiles along the tokens, so the cached codes are read, dequantized, transposed and quantized
+ * again ([W5], the chip-design passage on transposed reads that would spare these memory operations).
+ *   q_in  u8 [rows][cols], s_in f32 [cols/128][rows]: codes and scales of fg_quantize_act_1x128 along
+ *         the columns (row stride cols).
+ *   Each element is taken as the bf16 activation bf16(RN_f32(decoded code * its row scale)), and that
+ *   tensor is quantized as fg_quantize_act_1x128(.., FG_ALONG_ROWS, mode) would quantize it:
+ *   q_out u8 [cols][rows] (transposed), s_out f32 [rows/128][cols].
+ *   With power-of-2 scales in and out, the dequantized values lie on the E4M3 grid of every power-of-2
+ *   scale, so re-quantizing rounds nothing except values that leave E4M3's normal range; with fp32
+ *   scales each value is rounded a second time.
+ *   rows % 128 == 0, cols % 128 == 0. q_in, s_in, q_out 16-byte aligned; s_out 4-byte aligned.
+ *   rows == 0 or cols == 0 is a no-op. */
+fg_status fg_requantize_1x128_to_tokens(const uint8_t* q_in, const float* s_in, int64_t rows, int64_t cols,
+                                        fg_scale_mode mode, uint8_t* q_out, float* s_out, hipStream_t stream);
+
 /* 128x128 weight-block quantization ([W2]/[W3]/[W4], Figure 7 (a): per 128 input channels per 128
  * output channels).
  *   w       bf16 [n][k], row stride ld_w; k % 128 == 0; any n >= 0 (a short last block row-group takes

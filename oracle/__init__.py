@@ -34,6 +34,7 @@ def lib():
         L.oracle_scale_from_amax.argtypes = [ctypes.c_float, I]
         L.oracle_quantize_act_1x128.argtypes = [P, I64, I64, I64, I, I, P, P]
         L.oracle_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P]
+        L.oracle_requantize_1x128_to_tokens.argtypes = [P, P, I64, I64, I, P, P]
         L.oracle_amax_bf16.restype = ctypes.c_float
         L.oracle_amax_bf16.argtypes = [P, I64, I64, I64]
         L.oracle_quantize_per_tensor.argtypes = [P, I64, I64, I64, P, I64, I, I, P, P]
@@ -100,6 +101,18 @@ def quantize_w_128x128(w_bits, pow2: bool):
     s = np.empty(((n + 127) // 128, (k + 127) // 128), np.float32)
     lib().oracle_quantize_w_128x128(_p(w), n, k, k, int(pow2), _p(q), _p(s))
     return q, s
+
+
+def requantize_1x128_to_tokens(q, s, pow2: bool):
+    """Cached 1x128 codes q uint8 [rows, cols] with scales s f32 [cols/128, rows] -> token tiles of the bf16
+    activations they stand for: (q_out uint8 [cols, rows], s_out f32 [ceil(rows/128), cols])."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.float32)
+    rows, cols = q.shape
+    q_out = np.empty((cols, rows), np.uint8)
+    s_out = np.empty(((rows + 127) // 128, cols), np.float32)
+    lib().oracle_requantize_1x128_to_tokens(_p(q), _p(s), rows, cols, int(pow2), _p(q_out), _p(s_out))
+    return q_out, s_out
 
 
 def amax_bf16(x_bits):

@@ -30,6 +30,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <float.h>
 #include <omp.h>
@@ -181,6 +182,23 @@ void oracle_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t 
                 for (int64_t c = c0; c < c1; c++)
                     q[r * k + c] = oracle_e4m3_encode(oracle_bf16_to_f32(w[r * ld + c]) / s);
         }
+}
+
+/* Token tiles from cached FP8 activations: codes q [rows][cols] with their 1x128 row-tile scales
+ * s [cols/128][rows] stand for the bf16 activations bf16(RN_f32(dec(q) * s)) (activations kept in FP8 for
+ * the backward pass, [W4]/[W5] Figure 6 passage; dequantized in fp32 and stored back as the activation's
+ * bf16, the reading taken here), which are then quantized along the tokens as above (axis 1). */
+void oracle_requantize_1x128_to_tokens(const uint8_t* q, const float* s, int64_t rows, int64_t cols, int pow2,
+                                       uint8_t* q_out, float* s_out) {
+    uint16_t* x = (uint16_t*)malloc((size_t)(rows * cols) * sizeof(uint16_t));
+    if (!x) return;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++) {
+            float v = (float)oracle_e4m3_decode(q[r * cols + c]) * s[(c / GROUP) * rows + r];
+            x[r * cols + c] = oracle_f32_to_bf16(v);
+        }
+    oracle_quantize_act_1x128(x, rows, cols, cols, 1, pow2, q_out, s_out);
+    free(x);
 }
 
 /* ------------------------------------------------------------------------------------------------ */

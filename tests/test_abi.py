@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -140,3 +140,13 @@ def test_per_tensor_rejections(L):
     assert q(A16, 4, 128, 128, A16B, 4, 0, 0, A16, A16, A16B + 8, None) == INVALID  # amax_out inside history
     assert q(A16, 4, 128, 128, A16B, 1, 0, 0, ODD, A16, None, None) == MISALIGNED
     assert q(None, 0, 128, 128, None, 0, 0, 0, None, None, None, None) == OK       # empty
+
+
+def test_requantize_rejections(L):
+    r = L.fg_requantize_1x128_to_tokens
+    assert r(A16, A16, 100, 128, 0, A16, A16, None) == SHAPE            # rows % 128
+    assert r(A16, A16, 128, 200, 0, A16, A16, None) == SHAPE            # cols % 128
+    assert r(A16, A16, 128, 128, 7, A16, A16, None) == INVALID          # bad mode
+    assert r(A16, None, 128, 128, 0, A16, A16, None) == INVALID         # null input scales
+    assert r(A16, ODD, 128, 128, 0, A16, A16, None) == MISALIGNED       # input scales need 16 B
+    assert r(None, None, 0, 128, 0, None, None, None) == OK             # empty

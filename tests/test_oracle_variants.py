@@ -1,4 +1,5 @@
-"""Pins for the oracle's per-tensor scaling (the contrast baseline), CPU only.
+"""Pins for the oracle's variants of the tiles: per-tensor scaling (the contrast baseline) and token tiles
+re-quantized from cached 1x128 FP8 tiles. CPU only.
 
 Per-tensor scaling maps a whole tensor's max-abs onto the largest E4M3 value ("5 Ways You can get More
 Deepseek While Spending Less", the passage on the usual FP8 recipe and its outlier sensitivity); delayed
@@ -6,6 +7,11 @@ scaling takes that max-abs from a history of earlier iterations ("Three Fast Met
 the passage on delayed quantization). Pinned against library routines (numpy max, fp32 division, torch's
 E4M3 cast after clipping to +-448), against the tile quantizers on tensors that are one tile, and against
 closed forms of the scale and of saturation.
+
+Re-quantization reads activations cached as FP8 1x128 tiles for the backward pass (the Figure 6
+passage) and forms the token tiles Wgrad needs. Pinned against the composition through library routines
+(torch's E4M3 decode and bf16 cast, then the already pinned token-dim quantizer), and against the
+arithmetic fact that power-of-2 scales add no rounding in E4M3's normal range.
 """
 import numpy as np
 import pytest
@@ -131,3 +137,57 @@ def test_outliers_hurt_per_tensor_more_than_tiles():
     flushed = lambda q: ((q[:, ordinary] & 0x7F) == 0).mean()
     assert nsr(deq_t) < 0.03 and nsr(deq_p) > 1.5 * nsr(deq_t)
     assert flushed(qt) < 1e-4 and flushed(qp) > 0.01
+
+
+# ------------------------------------------------------------------------------------------------
+# Token tiles re-quantized from cached 1x128 FP8 tiles
+# ------------------------------------------------------------------------------------------------
+
+def _library_dequant_bf16(q, s):
+    """bf16 bits of bf16(RN_f32(decoded code * row scale)) through torch's E4M3 decode and bf16 cast."""
+    d = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float32)
+    sc = torch.from_numpy(np.repeat(s.T, 128, axis=1))
+    return (d * sc).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("pow2_in,pow2_out", [(False, False), (True, True), (False, True)])
+def test_requantize_is_token_quantization_of_the_cached_activation(pow2_in, pow2_out):
+    xb = _act(256, 384, 11, outliers=3)
+    q, s = oracle.quantize_act_1x128(xb, 0, pow2_in)
+    qt, st = oracle.requantize_1x128_to_tokens(q, s, pow2_out)
+    q2, s2 = oracle.quantize_act_1x128(_library_dequant_bf16(q, s), 1, pow2_out)
+    assert qt.shape == (384, 256) and st.shape == (2, 384)
+    assert np.array_equal(qt, q2) and np.array_equal(st, s2)
+
+
+def test_requantize_pow2_adds_no_rounding_in_the_normal_range():
+    """With power-of-2 scales the cached values are E4M3 numbers times 2^k; dividing by another power of
+    two keeps their 4 significant bits, so a re-quantized value equals the cached one wherever it stays
+    in E4M3's normal range."""
+    xb = _act(512, 256, 12, outliers=2)
+    q, s = oracle.quantize_act_1x128(xb, 0, True)
+    qt, st = oracle.requantize_1x128_to_tokens(q, s, True)
+    cached = oracle.e4m3_decode(q) * np.repeat(s.T, 128, axis=1)                  # [rows, cols]
+    requant = (oracle.e4m3_decode(qt) * np.repeat(st.T, 128, axis=1)).T          # back to [rows, cols]
+    normal = np.abs(cached) / np.repeat(st, 128, axis=0) >= 2.0 ** -6
+    assert normal.mean() > 0.95
+    assert np.array_equal(requant[normal], cached[normal])
+
+
+def test_requantize_fp32_scales_round_twice():
+    """With fp32 scales the re-quantized token tiles carry both roundings: their error against the original
+    activations exceeds that of token tiles quantized from the activations directly. With power-of-2
+    scales every orientation of the tiles rounds each value to the same 4 significant bits (normal range),
+    so the re-quantized, the direct token and the row tiles agree."""
+    xb = _act(512, 512, 13)
+    x = oracle.bf16_bits_to_f32(xb).astype(np.float64)
+    rms = lambda d: np.sqrt(((d - x) ** 2).mean() / (x ** 2).mean())
+    deq_t = lambda qq, ss: (oracle.e4m3_decode(qq) * np.repeat(ss.T, 128, axis=1)).T
+    errs = {}
+    for pow2 in (False, True):
+        q, s = oracle.quantize_act_1x128(xb, 0, pow2)
+        qt, st = oracle.requantize_1x128_to_tokens(q, s, pow2)
+        qd, sd = oracle.quantize_act_1x128(xb, 1, pow2)
+        errs[pow2] = (rms(deq_t(qt, st)), rms(deq_t(qd, sd)))
+    assert errs[False][0] > 1.2 * errs[False][1]
+    assert abs(errs[True][0] - errs[True][1]) < 1e-9
