@@ -313,6 +313,22 @@ def main():
             requant[tname] = {"shape": [rows, cols], "requant_ms": round(ms_r, 4), "requant_GB/s": round(gbps, 1),
                               "from_bf16_ms": round(ms_d, 4)}
 
+    # E5M6 storage of a cached activation (X): 2 B read + 1.5 B written per value to store, the reverse
+    # to load it back as bf16.
+    e5m6 = None
+    if not args.no_per_tensor:
+        pk = torch.empty((M, K * 3 // 2), dtype=u8, device=dev)
+        sk = torch.empty((K // 128, M), dtype=f32, device=dev)
+        yb = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        nbytes = M * K * 2 + M * K * 3 // 2 + M * K // 128 * 4
+        st = [("store", lambda: fg.fg_quantize_e5m6_1x128(x, packed=pk, scales=sk), "hbm", nbytes)]
+        ld_ = [("load", lambda: fg.fg_dequantize_e5m6_1x128(pk, sk, y=yb), "hbm", nbytes)]
+        ms_s, _ = measure(st, args.steps, args.warmup, "E5M6 storage of X")
+        ms_l, _ = measure(ld_, args.steps, args.warmup, "E5M6 load of X")
+        e5m6 = {"shape": [M, K], "store_ms": round(ms_s, 4), "store_GB/s": round(nbytes / (ms_s * 1e-3) / 1e9, 1),
+                "load_ms": round(ms_l, 4), "load_GB/s": round(nbytes / (ms_l * 1e-3) / 1e9, 1)}
+        del pk, sk, yb
+
     # Grouped MoE GEMM (one GPU's expert share): up-projection then down-projection, BF16 out.
     moe = None
     if not args.no_moe:
@@ -445,6 +461,7 @@ def main():
         "fprop_output_quantized": fused_epi,
         "per_tensor_contrast": per_tensor,
         "requantize_tokens": requant,
+        "e5m6_storage": e5m6,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out))

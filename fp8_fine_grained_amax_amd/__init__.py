@@ -44,12 +44,14 @@ def lib():
         L.fg_fp8_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_amax_bf16.argtypes = [P, I64, I64, I64, P, P]
+        L.fg_quantize_e5m6_1x128.argtypes = [P, I64, I64, I64, P, P, P]
+        L.fg_dequantize_e5m6_1x128.argtypes = [P, P, I64, I64, P, I64, P]
         L.fg_requantize_1x128_to_tokens.argtypes = [P, P, I64, I64, I, P, P, P]
         L.fg_quantize_per_tensor.argtypes = [P, I64, I64, I64, P, I64, I, I, P, P, P, P]
         for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop",
                   "fg_fp8_gemm_fprop_quant", "fg_fp8_gemm_dgrad", "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm",
                   "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad", "fg_amax_bf16", "fg_quantize_per_tensor",
-                  "fg_requantize_1x128_to_tokens"):
+                  "fg_requantize_1x128_to_tokens", "fg_quantize_e5m6_1x128", "fg_dequantize_e5m6_1x128"):
             getattr(L, f).restype = I
         L.fg_status_string.argtypes = [I]
         L.fg_status_string.restype = ctypes.c_char_p
@@ -172,6 +174,32 @@ def _bf16_2d(x, what):
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise Fp8fgError(f"{what} must be a 2-D bf16 tensor with unit column stride")
     return x.shape
+
+
+def fg_quantize_e5m6_1x128(x, packed=None, scales=None):
+    """E5M6 storage of a bf16 matrix x [rows, cols] in 1x128 tiles with power-of-2 scales: returns
+    (packed uint8 [rows, cols * 3 / 2], scales f32 [cols/128, rows])."""
+    rows, cols = _bf16_2d(x, "x")
+    if packed is None:
+        packed = torch.empty((rows, cols * 3 // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((cols // 128, rows), dtype=torch.float32, device=x.device)
+    _gpu(packed, scales)
+    _check(lib().fg_quantize_e5m6_1x128(_ptr(x), rows, cols, x.stride(0), _ptr(packed), _ptr(scales),
+                                        _stream(x.device)), "fg_quantize_e5m6_1x128")
+    return packed, scales
+
+
+def fg_dequantize_e5m6_1x128(packed, scales, y=None):
+    """bf16 [rows, cols] from E5M6 storage (packed uint8 [rows, cols * 3 / 2], scales f32 [cols/128, rows])."""
+    _gpu(packed, scales, y)
+    rows = packed.shape[0]
+    cols = packed.shape[1] * 2 // 3
+    if y is None:
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=packed.device)
+    _check(lib().fg_dequantize_e5m6_1x128(_ptr(packed), _ptr(scales), rows, cols, _ptr(y), y.stride(0),
+                                          _stream(packed.device)), "fg_dequantize_e5m6_1x128")
+    return y
 
 
 def fg_amax_bf16(x, amax=None):

@@ -34,6 +34,10 @@ hipError_t fg_launch_gemm_grouped(const uint8_t* xq, const float* sx, const uint
                                   const int32_t* offsets, int32_t G, int64_t T, int64_t N, int64_t K, void* y,
                                   int out_bf16, int pow2, hipStream_t stream);
 
+hipError_t fg_launch_quant_e5m6(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* packed,
+                                float* scales, hipStream_t stream);
+hipError_t fg_launch_dequant_e5m6(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols, uint16_t* y,
+                                  int64_t ldy, hipStream_t stream);
 hipError_t fg_launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax, hipStream_t stream);
 hipError_t fg_launch_quant_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* hist,
                                       int64_t n_hist, int pow2, int64_t n_scales, uint8_t* q, float* scales,
@@ -67,6 +71,28 @@ int64_t tiles(int64_t a, int64_t b) { return ((a + 255) / 256) * ((b + 127) / 12
 }  // namespace
 
 extern "C" {
+
+fg_status fg_quantize_e5m6_1x128(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* packed,
+                                 float* scales, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || ld_x < cols) return FG_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return FG_OK;
+    if (!x || !packed || !scales) return FG_ERR_INVALID_ARG;
+    if (cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(x) || (ld_x % 8) != 0 || !aligned4(packed) || !aligned4(scales)) return FG_ERR_MISALIGNED;
+    if ((cols / 128) * ((rows + 31) / 32) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    return from_hip(fg_launch_quant_e5m6((const uint16_t*)x, rows, cols, ld_x, packed, scales, stream));
+}
+
+fg_status fg_dequantize_e5m6_1x128(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols, void* y,
+                                   int64_t ld_y, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || ld_y < cols) return FG_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return FG_OK;
+    if (!packed || !scales || !y) return FG_ERR_INVALID_ARG;
+    if (cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(y) || (ld_y % 8) != 0 || !aligned4(packed) || !aligned4(scales)) return FG_ERR_MISALIGNED;
+    if ((cols / 128) * ((rows + 31) / 32) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    return from_hip(fg_launch_dequant_e5m6(packed, scales, rows, cols, (uint16_t*)y, ld_y, stream));
+}
 
 fg_status fg_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax, hipStream_t stream) {
     if (rows < 0 || cols < 0 || ld_x < cols) return FG_ERR_INVALID_ARG;

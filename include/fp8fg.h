@@ -215,6 +215,28 @@ fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, cons
                                     const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
                                     float* dw, int accumulate, fg_scale_mode scales, hipStream_t stream);
 
+/* ---- E5M6 storage of cached activations -------------------------------------------------------------
+ * [W1] keeps some cached activations (those entering the Linear after the attention operator) in a
+ * customized E5M6 format with power-of-2 scaling factors, and stores forward activations as 1x128 tiles.
+ * Format (a reading; the pages name it only): sign, 5 exponent bits with bias 15, 6 fraction bits;
+ * exponent 31 holds infinities and NaN as in E5M2 and binary16; largest finite value 65024; subnormals
+ * down to 2^-20. Encoding rounds to nearest even and saturates at +-65024, keeping the sign.
+ * Packing: two 12-bit codes c0, c1 per 3 bytes, little-endian: byte0 = c0 & 0xFF,
+ * byte1 = (c0 >> 8) | ((c1 & 0xF) << 4), byte2 = c1 >> 4; a row of cols values takes cols * 3 / 2 bytes. */
+
+/* x bf16 [rows][cols] (row stride ld_x) -> packed u8 [rows][cols * 3 / 2] and scales f32 [cols/128][rows].
+ * Per 1x128 tile: s = the smallest power of two >= RN_f32(max-abs / 65024) (max-abs 0 gives 1; scales
+ * below FLT_MIN become FLT_MIN); codes encode x / s (exact). cols % 128 == 0, any rows.
+ * x 16-byte aligned, ld_x % 8 == 0; packed 4-byte aligned; scales 4-byte aligned. rows == 0: no-op. */
+fg_status fg_quantize_e5m6_1x128(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* packed,
+                                 float* scales, hipStream_t stream);
+
+/* packed, scales as written by fg_quantize_e5m6_1x128 -> y bf16 [rows][cols] (row stride ld_y):
+ * y = bf16(RN_f32(decoded code * s)), exact for every value inside bf16's range.
+ * cols % 128 == 0; y 16-byte aligned, ld_y % 8 == 0, ld_y >= cols; packed, scales 4-byte aligned. */
+fg_status fg_dequantize_e5m6_1x128(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols, void* y,
+                                   int64_t ld_y, hipStream_t stream);
+
 /* ---- Per-tensor scaling: the contrast baseline ----------------------------------------------------
  * The usual FP8 recipe that the fine-grained tiles replace ([W1], the passage on aligning a whole
  * tensor's max-abs to the largest FP8 value and on its sensitivity to activation outliers) and its

@@ -35,6 +35,12 @@ def lib():
         L.oracle_quantize_act_1x128.argtypes = [P, I64, I64, I64, I, I, P, P]
         L.oracle_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P]
         L.oracle_requantize_1x128_to_tokens.argtypes = [P, P, I64, I64, I, P, P]
+        L.oracle_e5m6_decode.restype = ctypes.c_double
+        L.oracle_e5m6_decode.argtypes = [ctypes.c_uint16]
+        L.oracle_e5m6_encode.restype = ctypes.c_uint16
+        L.oracle_e5m6_encode.argtypes = [ctypes.c_float]
+        L.oracle_quantize_e5m6_1x128.argtypes = [P, I64, I64, I64, P, P]
+        L.oracle_dequantize_e5m6_1x128.argtypes = [P, P, I64, I64, P]
         L.oracle_amax_bf16.restype = ctypes.c_float
         L.oracle_amax_bf16.argtypes = [P, I64, I64, I64]
         L.oracle_quantize_per_tensor.argtypes = [P, I64, I64, I64, P, I64, I, I, P, P]
@@ -113,6 +119,47 @@ def requantize_1x128_to_tokens(q, s, pow2: bool):
     s_out = np.empty(((rows + 127) // 128, cols), np.float32)
     lib().oracle_requantize_1x128_to_tokens(_p(q), _p(s), rows, cols, int(pow2), _p(q_out), _p(s_out))
     return q_out, s_out
+
+
+def e5m6_decode(codes):
+    """Values of 12-bit E5M6 codes (array), float64."""
+    c = np.asarray(codes, np.uint16)
+    table = np.array([lib().oracle_e5m6_decode(i) for i in range(4096)], np.float64)
+    return table[c & 0xFFF]
+
+
+def e5m6_encode(values):
+    """E5M6 codes of float32 values (array)."""
+    v = np.asarray(values, np.float32).reshape(-1)
+    return np.array([lib().oracle_e5m6_encode(float(f)) for f in v], np.uint16).reshape(np.shape(values))
+
+
+def quantize_e5m6_1x128(x_bits):
+    """bf16 bits [rows, cols] -> (packed uint8 [rows, cols * 3 / 2], scales f32 [cols/128, rows])."""
+    x = _u16(x_bits)
+    rows, cols = x.shape
+    packed = np.empty((rows, cols * 3 // 2), np.uint8)
+    s = np.empty((cols // 128, rows), np.float32)
+    lib().oracle_quantize_e5m6_1x128(_p(x), rows, cols, cols, _p(packed), _p(s))
+    return packed, s
+
+
+def dequantize_e5m6_1x128(packed, scales):
+    """bf16 bits [rows, cols] that E5M6 storage stands for."""
+    packed = np.ascontiguousarray(packed, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    rows, cols = packed.shape[0], packed.shape[1] * 2 // 3
+    y = np.empty((rows, cols), np.uint16)
+    lib().oracle_dequantize_e5m6_1x128(_p(packed), _p(scales), rows, cols, _p(y))
+    return y
+
+
+def e5m6_unpack(packed):
+    """12-bit codes [rows, cols] from packed [rows, cols * 3 / 2] (three bytes per two codes)."""
+    p = np.asarray(packed, np.uint16).reshape(packed.shape[0], -1, 3)
+    c0 = p[..., 0] | ((p[..., 1] & 0xF) << 8)
+    c1 = (p[..., 1] >> 4) | (p[..., 2] << 4)
+    return np.stack([c0, c1], axis=-1).reshape(packed.shape[0], -1)
 
 
 def amax_bf16(x_bits):

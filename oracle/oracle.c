@@ -202,6 +202,93 @@ void oracle_requantize_1x128_to_tokens(const uint8_t* q, const float* s, int64_t
 }
 
 /* ------------------------------------------------------------------------------------------------ */
+/* E5M6 storage of cached activations                                                               */
+/* ------------------------------------------------------------------------------------------------ */
+
+/* [W1] names a customized E5M6 format for some cached activations, with power-of-2 scaling factors.
+ * Reading R16: 12-bit code s eeeee mmmmmm, exponent bias 15, exponent 31 holds infinities (fraction 0) and
+ * NaN as in the other E5 formats, subnormals m * 2^-20; largest finite (2 - 2^-6) * 2^15 = 65024. */
+double oracle_e5m6_decode(uint16_t code) {
+    int s = (code >> 11) & 1, e = (code >> 6) & 31, m = code & 63;
+    double mag;
+    if (e == 31) mag = m ? NAN : INFINITY;
+    else if (e == 0) mag = ldexp((double)m, -20);
+    else mag = ldexp(1.0 + m / 64.0, e - 15);
+    return s ? -mag : mag;
+}
+
+/* Nearest E5M6 value, ties to the even fraction, magnitudes above 65024 saturate, sign kept (R16).
+ * Written like the E4M3 encoder: the spacing near |v| is 2^-20 below 2^-14 and 2^(floor(log2|v|) - 6)
+ * above; |v| / spacing is rounded to the nearest integer with ties to even. */
+uint16_t oracle_e5m6_encode(float v) {
+    uint16_t sign = signbit(v) ? 0x800 : 0;
+    double a = fabs((double)v);
+    if (a >= 65024.0) return sign | 0x7BF;
+    double q;
+    if (a < ldexp(1.0, -14)) {
+        q = ldexp(1.0, -20);
+    } else {
+        int e;
+        frexp(a, &e);
+        q = ldexp(1.0, (e - 1) - 6);
+    }
+    double r = nearbyint(a / q), val = r * q;
+    if (val == 0.0) return sign;
+    if (val < ldexp(1.0, -14)) return sign | (uint16_t)r;       /* subnormal: fraction = r (1..63)    */
+    if (val >= 65024.0) return sign | 0x7BF;
+    int e2;
+    double f2 = frexp(val, &e2);
+    int exp_field = (e2 - 1) + 15;
+    int mant = (int)((2.0 * f2 - 1.0) * 64.0);
+    return sign | (uint16_t)(exp_field << 6) | (uint16_t)mant;
+}
+
+/* 1x128 tiles along the columns with power-of-2 scales ([W1], opening paragraph): s = the smallest power
+ * of two >= RN_f32(amax / 65024) (R3/R4 with the E5M6 maximum); codes enc(x / s), packed two per three
+ * bytes, little-endian (byte 0: c0 bits 0-7; byte 1: c0 bits 8-11, c1 bits 0-3; byte 2: c1 bits 4-11).
+ * x [rows][cols] -> packed [rows][cols * 3 / 2], scales [cols/128][rows]; cols a multiple of 128. */
+void oracle_quantize_e5m6_1x128(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* packed,
+                                float* scales) {
+    int64_t ngroups = cols / GROUP, ldp = cols * 3 / 2;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t g = 0; g < ngroups; g++) {
+            float amax = amax_of(x + r * ld + g * GROUP, 1, GROUP, ld);
+            float s = 1.0f;
+            if (amax != 0.0f) {
+                s = amax / 65024.0f;
+                if (s < FLT_MIN) s = FLT_MIN;
+                int e;
+                float f = frexpf(s, &e);
+                if (f != 0.5f) s = ldexpf(1.0f, e);
+            }
+            scales[g * rows + r] = s;
+            for (int64_t c = g * GROUP; c < (g + 1) * GROUP; c += 2) {
+                uint16_t c0 = oracle_e5m6_encode(oracle_bf16_to_f32(x[r * ld + c]) / s);
+                uint16_t c1 = oracle_e5m6_encode(oracle_bf16_to_f32(x[r * ld + c + 1]) / s);
+                uint8_t* p = packed + r * ldp + (c / 2) * 3;
+                p[0] = (uint8_t)(c0 & 0xFF);
+                p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xF) << 4));
+                p[2] = (uint8_t)(c1 >> 4);
+            }
+        }
+}
+
+/* The bf16 values E5M6 storage stands for: bf16(RN_f32(dec(code) * s)). */
+void oracle_dequantize_e5m6_1x128(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols,
+                                  uint16_t* y) {
+    int64_t ldp = cols * 3 / 2;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c += 2) {
+            const uint8_t* p = packed + r * ldp + (c / 2) * 3;
+            uint16_t c0 = (uint16_t)(p[0] | ((p[1] & 0xF) << 8));
+            uint16_t c1 = (uint16_t)((p[1] >> 4) | (p[2] << 4));
+            float s = scales[(c / GROUP) * rows + r];
+            y[r * cols + c] = oracle_f32_to_bf16((float)oracle_e5m6_decode(c0) * s);
+            y[r * cols + c + 1] = oracle_f32_to_bf16((float)oracle_e5m6_decode(c1) * s);
+        }
+}
+
+/* ------------------------------------------------------------------------------------------------ */
 /* Per-tensor scaling: the prior practice the tiles are contrasted with                             */
 /* ------------------------------------------------------------------------------------------------ */
 

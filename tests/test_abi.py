@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -150,3 +150,19 @@ def test_requantize_rejections(L):
     assert r(A16, None, 128, 128, 0, A16, A16, None) == INVALID         # null input scales
     assert r(A16, ODD, 128, 128, 0, A16, A16, None) == MISALIGNED       # input scales need 16 B
     assert r(None, None, 0, 128, 0, None, None, None) == OK             # empty
+
+
+def test_e5m6_rejections(L):
+    q = L.fg_quantize_e5m6_1x128
+    assert q(A16, 4, 200, 200, A16, A16, None) == SHAPE                 # cols % 128
+    assert q(A16, 4, 128, 100, A16, A16, None) == INVALID               # ld < cols
+    assert q(A16, 4, 128, 128, None, A16, None) == INVALID              # null packed
+    assert q(ODD, 4, 128, 128, A16, A16, None) == MISALIGNED
+    assert q(A16, 4, 128, 132, A16, A16, None) == MISALIGNED            # ld % 8
+    assert q(None, 0, 128, 128, None, None, None) == OK                 # empty
+    d = L.fg_dequantize_e5m6_1x128
+    assert d(A16, A16, 4, 200, A16, 200, None) == SHAPE
+    assert d(A16, A16, 4, 128, A16, 100, None) == INVALID               # ld < cols
+    assert d(A16, None, 4, 128, A16, 128, None) == INVALID              # null scales
+    assert d(A16, A16, 4, 128, ODD, 128, None) == MISALIGNED
+    assert d(None, None, 0, 128, None, 128, None) == OK
