@@ -164,39 +164,72 @@ def main():
              "mfma", 2.0 * M * N * K),
         ]
 
-    def measure(ops, steps, warmup, tag):
-        """W untimed steps, then exactly `steps` timed steps between two device synchronisations; HIP events
-        recorded on the kernels' own stream around every launch give the per-kernel times."""
-        def run_step(events=None):
-            for i, (_, fn, _, _) in enumerate(ops):
-                if events is not None:
-                    events[i][0].record(stream)
-                fn()
-                if events is not None:
-                    events[i][1].record(stream)
+    def run_step(ops, events=None):
+        for i, (_, fn, _, _) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
 
+    def measure(ops, steps, warmup, tag):
+        """W untimed steps, then exactly `steps` timed steps between two device synchronisations (the step
+        time); then `steps` more with HIP events recorded on the kernels' own stream around every launch
+        (the per-kernel times; the events are kept out of the step time)."""
         for _ in range(warmup):
-            run_step()
-        torch.cuda.synchronize()
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-              for _ in range(steps)]
+            run_step(ops)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(steps):
-            run_step(ev[s])
+        for _ in range(steps):
+            run_step(ops)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms = (t1 - t0) * 1e3 / steps
-        per = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+              for _ in range(steps)]
+        for s_ in range(steps):
+            run_step(ops, ev[s_])
+        torch.cuda.synchronize()
+        per = {name: float(np.mean([ev[s_][i][0].elapsed_time(ev[s_][i][1]) for s_ in range(steps)]))
                for i, (name, _, _, _) in enumerate(ops)}
         print(f"[bench] {tag}: timed {steps} steps after {warmup} warmup: {ms:.3f} ms/step", file=sys.stderr,
               flush=True)
         return ms, per
 
+    def measure_graph(ops, steps, warmup, tag):
+        """The same step captured once in a HIP graph and replayed: W untimed replays, then exactly `steps`
+        timed replays between two device synchronisations."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_step(ops)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        print(f"[bench] {tag} (HIP graph): timed {steps} replays after {warmup} warmup: {ms:.3f} ms/step",
+              file=sys.stderr, flush=True)
+        return g, ms
+
     POW2 = bool(args.pow2)
     ops = make_ops(POW2, fused=True)
-    ms_per_step, per_kernel_ms = measure(ops, args.steps, args.warmup,
-                                         ("pow2" if POW2 else "fp32") + " scales, fused quantizers")
+    ms_eager, per_kernel_ms = measure(ops, args.steps, args.warmup,
+                                      ("pow2" if POW2 else "fp32") + " scales, fused quantizers")
+    # The step as one HIP graph: its outputs must equal the eager step's bit for bit before its time counts.
+    outs = ("y", "dx", "dw", "xq", "sx", "xtq", "sxt", "wq", "sw", "dyq", "sdy", "dytq", "sdyt")
+    run_step(ops)
+    torch.cuda.synchronize()
+    eager_out = {k: B[k].clone() for k in outs}
+    for k in outs:
+        B[k].zero_()
+    graph, ms_graph = measure_graph(ops, args.steps, args.warmup, ("pow2" if POW2 else "fp32") + " scales, fused quantizers")
+    torch.cuda.synchronize()
+    graph_ok = all(torch.equal(B[k].view(torch.uint8), eager_out[k].view(torch.uint8)) for k in outs)
+    del eager_out, graph
+    ms_per_step = ms_graph if graph_ok and ms_graph < ms_eager else ms_eager
+    launch_mode = "hip_graph" if ms_per_step == ms_graph else "eager"
     # Other variants of the same step on the same buffers, reported beside the headline: the other scale
     # mode, and one launch per tiling instead of the fused quantizers.
     variants = {}
@@ -445,7 +478,8 @@ def main():
         "config": {"workload": "dsv3_dense_mlp_linear_fwd_bwd", "M_tokens": M, "N_out": N, "K_in": K,
                    "tiles": "1x128 activations, 128x128 weights", "scale_mode": "pow2" if POW2 else "fp32",
                    "quantizers": "fused (X and dY read once for both tilings)", "accumulate": "fp32, promoted every 128 K",
-                   "fprop_out": "bf16", "dgrad_out": "f32", "wgrad_out": "f32"},
+                   "fprop_out": "bf16", "dgrad_out": "f32", "wgrad_out": "f32", "launch": launch_mode},
+        "step_ms": {"eager": round(ms_eager, 4), "hip_graph": round(ms_graph, 4), "hip_graph_matches_eager": graph_ok},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "quantize_GBps_in_step": round(qbytes / (qms * 1e-3) / 1e9, 1),
