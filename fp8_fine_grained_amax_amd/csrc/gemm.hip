@@ -40,6 +40,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "host_util.h"
 
 namespace {
 
@@ -615,12 +616,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
 template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE>
 hipError_t launch_one(const GemmParams& p, unsigned grid, hipStream_t stream) {
     auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUP, POW2, EPI>;
-    static bool attr_set = false;   // benign race: setting the attribute twice is harmless
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_limit_set{0};
+    const hipError_t e = fg_set_lds_limit_once((const void*)kern, C::LDS_BYTES, lds_limit_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NTHREADS), C::LDS_BYTES, stream, p);
     return hipGetLastError();
 }
@@ -634,15 +632,6 @@ unsigned grid_for(const GemmParams& p, int group) {
     return (unsigned)(m_tiles * n_tiles);
 }
 
-// Compute units of the current device (the tile count that fills one round).
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus <= 0)
-        return 256;
-    return cus;
-}
-
 // Workgroup shape for one launch: the one with the smaller estimated time, counting full rounds of tiles
 // over the compute units, a tile's work (BM * BN) and the measured per-tile rate of the 8-wave shape
 // (about 6% more MFMA throughput per CU). FG_GEMM_TILE=256x192 or 256x256 in the environment forces a
@@ -651,7 +640,7 @@ bool use_cfg8(const GemmParams& p, int grouped) {
     const char* force = getenv("FG_GEMM_TILE");
     if (force && strcmp(force, "256x256") == 0) return true;
     if (force && strcmp(force, "256x192") == 0) return false;
-    const int64_t cus = device_cus();
+    const int64_t cus = fg_device_cus();
     const int64_t r12 = (grid_for<Cfg12>(p, grouped) + cus - 1) / cus;
     const int64_t r8 = (grid_for<Cfg8>(p, grouped) + cus - 1) / cus;
     return (double)r8 * Cfg8::BM * Cfg8::BN / 1.06 < (double)r12 * Cfg12::BM * Cfg12::BN;

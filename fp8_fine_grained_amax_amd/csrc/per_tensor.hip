@@ -13,6 +13,7 @@
 // 1x128 activation or 128x128 weight scale layout, so the block-scaled GEMMs consume these codes as
 // they are. The kernel can fold the tensor's own max-abs into a history slot on the way.
 #include "common.h"
+#include "host_util.h"
 
 namespace {
 
@@ -146,10 +147,7 @@ __global__ __launch_bounds__(kThreads) void fg_quant_per_tensor_kernel(const uin
 // One workgroup of 1024 lanes per compute unit (fewer for short tensors): 64 KB of loads in flight per
 // CU, and at most one max-abs atomic per CU.
 unsigned grid_rows(int64_t rows) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus <= 0)
-        cus = 256;
+    const int cus = fg_device_cus();
     return (unsigned)(rows < cus ? rows : cus);
 }
 
