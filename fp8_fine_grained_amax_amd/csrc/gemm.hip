@@ -480,9 +480,16 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                     sa_prev = sa_i;
                 }
             } else {
-                v4f prev = v4f{0.f, 0.f, 0.f, 0.f};
-                float s_prev[4] = {0.f, 0.f, 0.f, 0.f};
-                int ip = -1, jp = -1;
+                // Tile-lagged promotion: the FMAs issued after MFMA t fold tile t - LAG, whose result is long
+                // complete. Per-row B scales (two scale products per element) take the deeper lag where the
+                // registers allow it (8-wave shape); measured 3-4% faster on Wgrad than folding tile t - 1,
+                // and neutral on the 256x192 Fprop.
+                constexpr int LAG = SBK == SB_ROW && C::NW == 8 ? 3 : 2;
+                v4f pend[LAG];
+                float pend_s[LAG][4];
+                int pend_i[LAG], pend_j[LAG];
+#pragma unroll
+                for (int l = 0; l < LAG; l++) pend_i[l] = -1;
 #pragma unroll
                 for (int i = 0; i < MSUB; i++) {
                     issue_piece(kb1, st ^ 1, i);
@@ -492,27 +499,40 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                     for (int j = 0; j < NSUB; j++) {
                         const v4f cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             bf[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-                        if (ip >= 0) {
+                        constexpr int O = LAG - 1;    // the oldest pending tile
+                        if (pend_i[O] >= 0) {
 #pragma unroll
                             for (int r = 0; r < 4; r++)
-                                acc[ip][jp][r] = __builtin_fmaf(prev[r], s_prev[r], acc[ip][jp][r]);
+                                acc[pend_i[O]][pend_j[O]][r] =
+                                    __builtin_fmaf(pend[O][r], pend_s[O][r], acc[pend_i[O]][pend_j[O]][r]);
                         }
-                        prev = cur;
-                        ip = i;
-                        jp = j;
+#pragma unroll
+                        for (int l = O; l > 0; l--) {
+                            pend[l] = pend[l - 1];
+                            pend_i[l] = pend_i[l - 1];
+                            pend_j[l] = pend_j[l - 1];
+#pragma unroll
+                            for (int r = 0; r < 4; r++) pend_s[l][r] = pend_s[l - 1][r];
+                        }
+                        pend[0] = cur;
+                        pend_i[0] = i;
+                        pend_j[0] = j;
                         if constexpr (SBK != SB_ROW) {
                             const float s_ij = sa_i * sb_blk;
-                            s_prev[0] = s_prev[1] = s_prev[2] = s_prev[3] = s_ij;
+                            pend_s[0][0] = pend_s[0][1] = pend_s[0][2] = pend_s[0][3] = s_ij;
                         } else {
-                            s_prev[0] = sa_i * sbr[j].x;
-                            s_prev[1] = sa_i * sbr[j].y;
-                            s_prev[2] = sa_i * sbr[j].z;
-                            s_prev[3] = sa_i * sbr[j].w;
+                            pend_s[0][0] = sa_i * sbr[j].x;
+                            pend_s[0][1] = sa_i * sbr[j].y;
+                            pend_s[0][2] = sa_i * sbr[j].z;
+                            pend_s[0][3] = sa_i * sbr[j].w;
                         }
                     }
                 }
 #pragma unroll
-                for (int r = 0; r < 4; r++) acc[ip][jp][r] = __builtin_fmaf(prev[r], s_prev[r], acc[ip][jp][r]);
+                for (int l = LAG - 1; l >= 0; l--)
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[pend_i[l]][pend_j[l]][r] = __builtin_fmaf(pend[l][r], pend_s[l][r], acc[pend_i[l]][pend_j[l]][r]);
             }
         }
     }
