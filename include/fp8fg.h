@@ -2,8 +2,10 @@
  * fp8fg — fine-grained FP8 (OCP E4M3) quantization and block-scaled GEMMs for MI355X (gfx950).
  *
  * C ABI. Every pointer argument is DEVICE memory owned by the caller; the library never allocates, frees
- * or synchronises. All work is enqueued asynchronously on `stream` (0 = the null stream). The library keeps
- * no state between calls and is safe to call from several threads. Arguments are checked on the host
+ * or synchronises. All work is enqueued asynchronously on `stream` (0 = the null stream), and the calls
+ * can be captured in a HIP graph (no memset or host synchronisation is enqueued). The library keeps no
+ * state between calls beyond per-device facts cached on first use (compute-unit count, the GEMM kernels'
+ * LDS limit), and is safe to call from several threads. Arguments are checked on the host
  * before any HIP call; a failed check returns a status and enqueues nothing. A launch failure returns
  * FG_ERR_HIP and fg_last_hip_error() gives the hipError_t on the calling thread.
  *
@@ -49,7 +51,8 @@
  * scale product and no VALU work. Passing FG_SCALE_POW2 with other scales gives unspecified results.
  *
  * Every GEMM picks one of two workgroup tiles per launch (256x192 or 256x256 outputs) from the problem size
- * and the device's compute-unit count; results agree to the same tolerance either way. The environment
+ * and the device's compute-unit count; the results are bit-identical either way (every output element
+ * goes through the same instructions in the same order). The environment
  * variable FG_GEMM_TILE=256x192 or FG_GEMM_TILE=256x256 forces one (read at every launch).
  *
  * Layouts are row-major. "ld" arguments are row strides in elements.
