@@ -412,3 +412,40 @@ def test_grouped_wgrad_moe_share_sampled(pow2):
     device()
     d = wl.moe_backward_inputs()
     _grouped_wgrad_case(d["dy"], d["x"], d["offsets"], pts_per_group=300, pow2=pow2)
+
+
+# ------------------------------------------------------------------------------------------------
+# The two workgroup shapes give bit-identical results
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_tile_shapes_bit_identical(pow2, monkeypatch):
+    """Every output element goes through the same instructions in the same order under either workgroup
+    shape, so Fprop, Dgrad, Wgrad and grouped Fprop outputs must match bit for bit (ragged shapes)."""
+    device()
+    rng = np.random.default_rng(81)
+    M, N, K = 300, 520, 640
+    x = to_dev(_rand_act(rng, M, K))
+    w = to_dev(wl.normal_bf16(rng, (N, K), 0.02))
+    dy = to_dev(wl.normal_bf16(rng, (M, 384), 1e-3))
+    wd = to_dev(wl.normal_bf16(rng, (384, K), 0.02))
+    xq, sx = fg.fg_quantize_act_1x128(x, pow2=pow2)
+    wq, sw = fg.fg_quantize_w_128x128(w, pow2=pow2)
+    dyq, sdy = fg.fg_quantize_act_1x128(dy, pow2=pow2)
+    wdq, swd = fg.fg_quantize_w_128x128(wd, pow2=pow2)
+    xr = to_dev(_rand_act(rng, 384, 264))
+    dyr = to_dev(wl.normal_bf16(rng, (384, 200), 1e-3))
+    dytq, sdyt = fg.fg_quantize_act_1x128(dyr, axis=fg.FG_ALONG_ROWS, pow2=pow2)
+    xtq, sxt = fg.fg_quantize_act_1x128(xr, axis=fg.FG_ALONG_ROWS, pow2=pow2)
+    off = torch.tensor([0, 100, 100, 300], dtype=torch.int32, device=device())
+    wg, swg = torch.stack([wq, wq, wq]), torch.stack([sw, sw, sw])
+    outs = {}
+    for t in ("256x192", "256x256"):
+        monkeypatch.setenv("FG_GEMM_TILE", t)
+        outs[t] = [fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.float32, pow2=pow2),
+                   fg.fg_fp8_gemm_dgrad(dyq, sdy, wdq, swd, pow2=pow2),
+                   fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, pow2=pow2),
+                   fg.fg_fp8_grouped_gemm(xq, sx, wg, swg, off, out_dtype=torch.float32, pow2=pow2)]
+        torch.cuda.synchronize()
+    for name, a, b in zip(("fprop", "dgrad", "wgrad", "grouped"), outs["256x192"], outs["256x256"]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
