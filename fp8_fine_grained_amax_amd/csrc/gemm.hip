@@ -123,6 +123,15 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* tile16, int lo_off, int hi
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8, each XCD with its
+// own L2). Map workgroup b of a grid of `total` to a logical tile id so that every XCD holds one contiguous
+// range of ids: XCD x gets ids [x * (total / 8) + min(x, total % 8), ...), one per workgroup it runs.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+    const int x = b & 7, local = b >> 3;
+    const int base = total >> 3, extra = total & 7;
+    return x * base + (x < extra ? x : extra) + local;
+}
+
 // E8M0 code of an fp32 power of two in [2^-127, 2^127]: its biased exponent field.
 __device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23) & 0xFF; }
 
@@ -154,6 +163,8 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         // contraction, a whole number of 128-blocks
         const int m_tiles = (int)((p.M + BM - 1) / BM);
         const int tpg = m_tiles * n_tiles;
+        // consecutive workgroups (different XCDs) share a group: the groups' contraction lengths differ
+        // widely, and keeping one group on one XCD would leave that XCD with the longest tiles
         const int g = blockIdx.x / tpg;
         const int local = blockIdx.x % tpg;
         const int64_t seg0 = p.offsets[g], seg1 = p.offsets[g + 1];
@@ -169,8 +180,18 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         SBp += kb0 * N;
         outp = reinterpret_cast<float*>(p.out) + (int64_t)g * p.out_group_stride;
     } else if constexpr (GROUP == GRP_ROWS) {
-        const int id_m = blockIdx.x / n_tiles;
-        const int nt = blockIdx.x % n_tiles;
+        // Grouped Fprop: rows of N tiles are dealt to the XCDs in turn (row k to XCD k % 8), so an XCD keeps
+        // an M tile's N tiles together and the trailing no-op ids of the worst-case grid (a multiple of 8
+        // rows) spread over all XCDs; 3-4% faster on the MoE up-projection. Grouped Dgrad keeps the launch
+        // order, which deals an M tile's N tiles over the XCDs: each XCD then reuses its share of the
+        // transposed weight panel across M tiles (2-3% faster there than dealing whole rows).
+        int id = (int)blockIdx.x;
+        if constexpr (!B_TRANS) {
+            const int b = id, x = b & 7, j = b >> 3;
+            id = ((j / n_tiles) * 8 + x) * n_tiles + j % n_tiles;
+        }
+        const int id_m = id / n_tiles;
+        const int nt = id % n_tiles;
         int g = 0, cum = 0;
         int64_t seg0 = 0, seg1 = 0;
         for (; g < p.G; g++) {
@@ -189,10 +210,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     } else {
         const int m_tiles = (int)((p.M + BM - 1) / BM);
         const int total = m_tiles * n_tiles;
-        int id = blockIdx.x;
-        // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous range of
-        // logical tiles so the tiles it runs at the same time share A and B panels in its own L2.
-        if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+        // each XCD runs a contiguous range of logical tiles, so the tiles it runs at the same time share A
+        // and B panels in its own L2
+        const int id = xcd_remap((int)blockIdx.x, total);
         // groups of GM M tiles: tiles in flight together on an XCD form a compact block of the output (4 x 8
         // tiles of 256x192 and 8 x 4 tiles of 256x256 are the near-square blocks; both measured best)
         const int GM = C::NW == 12 ? 4 : 8;
@@ -647,7 +667,7 @@ template <class C>
 unsigned grid_for(const GemmParams& p, int group) {
     const int64_t n_tiles = (p.N + C::BN - 1) / C::BN;
     const int64_t m_tiles = (p.M + C::BM - 1) / C::BM;
-    if (group == GRP_ROWS) return (unsigned)((m_tiles + p.G) * n_tiles);   // worst case over the offsets
+    if (group == GRP_ROWS) return (unsigned)(((m_tiles + p.G + 7) / 8) * 8 * n_tiles);   // worst case, 8-row multiple
     if (group == GRP_K) return (unsigned)(m_tiles * n_tiles * p.G);
     return (unsigned)(m_tiles * n_tiles);
 }
