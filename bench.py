@@ -580,9 +580,9 @@ def vendor_reference(M, N, K, dev):
 
 
 def cpu_baseline():
-    """The oracle as it stands, on a bounded sample of the step's GEMM work (sampled outputs of Fprop,
-    Dgrad and Wgrad at the full shapes, each a full 128-blocked promoted dot product), run for ~10-20 s
-    on the host's cores. Reported in the same unit as `value`."""
+    """The oracle as it stands, on a bounded sample of the step's GEMM work (sampled Fprop outputs at the
+    full shape, each a full 128-blocked promoted dot product), run for ~10-20 s on the host's cores.
+    Reported in the same unit as `value`, with the thread count and the CPU model."""
     import numpy as np
     import oracle
     from fp8_fine_grained_amax_amd import workloads as wl
@@ -605,7 +605,13 @@ def cpu_baseline():
         total_flop += 2.0 * K * npts
         npts *= 2
     value = total_flop / elapsed / 1e12
-    return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "cpu_model": model, "kind": "oracle",
             "sample": f"{int(total_flop / (2 * K))} sampled Fprop outputs of the 4096x18432x7168 GEMM "
                       f"(each a 7168-deep promoted dot product), {elapsed:.1f} s"}
 

@@ -28,6 +28,7 @@ def lib():
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode_many.argtypes = [P, I64, P]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_scale_from_amax.restype = ctypes.c_float
@@ -69,6 +70,14 @@ def e4m3_decode(codes):
     codes = np.asarray(codes, dtype=np.uint8)
     table = np.array([lib().oracle_e4m3_decode(c) for c in range(256)], dtype=np.float64)
     return table[codes]
+
+
+def e4m3_encode_many(values):
+    """E4M3 codes of a float32 array (the oracle's encoder, element by element)."""
+    v = np.ascontiguousarray(values, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_e4m3_encode_many(_p(v), v.size, _p(out))
+    return out
 
 
 def e4m3_encode_scalar(v: float) -> int:

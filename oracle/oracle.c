@@ -77,6 +77,12 @@ uint8_t oracle_e4m3_encode(float v) {
     return sign | (uint8_t)(exp_field << 3) | (uint8_t)mant;
 }
 
+/* oracle_e4m3_encode over an array (for the exhaustive checks of the tests). */
+void oracle_e4m3_encode_many(const float* v, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_encode(v[i]);
+}
+
 float oracle_bf16_to_f32(uint16_t b) {
     uint32_t u = (uint32_t)b << 16;
     float f;

@@ -84,3 +84,22 @@ def test_promotion_beats_limited_accumulator():
     assert errs[16384]["limited_p10"] > errs[4096]["limited_p10"]  # grows with K
     for K in (4096, 16384):
         assert errs[K]["gpu_promoted"] * 100 < errs[K]["limited_p14"]
+
+
+@pytest.mark.parametrize("K", [4096, 16384])
+def test_hardware_chain_per_tensor_scale(K):
+    """gfx950's own accumulation: one scale for each whole operand (per-tensor, a power of two), so the scaled
+    MFMA carries a single FP32 accumulator across all of K with identical block scales. Elementwise error
+    against the exact value of the same codes."""
+    device()
+    x, w = wl.accumulation_stress(K)
+    xd, wd = to_dev(x), to_dev(w)
+    xq, sx = fg.fg_quantize_per_tensor(xd, fg.fg_amax_bf16(xd), pow2=True)
+    wq, sw = fg.fg_quantize_per_tensor(wd, fg.fg_amax_bf16(wd), pow2=True, layout=fg.FG_LAYOUT_W_128x128)
+    y = fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.float32, pow2=True)
+    torch.cuda.synchronize()
+    pts = sample_points(1024, 1024, 4000, seed=47)
+    _, exact = oracle.gemm_fprop(np_u8(xq), sx.cpu().numpy(), np_u8(wq), sw.cpu().numpy(), pts=pts)
+    rel = np.max(np.abs(y.cpu().numpy().reshape(-1)[pts].astype(np.float64) - exact) / np.abs(exact))
+    print(f"\n[accum] K={K} hardware chain, per-tensor power-of-2 scales: elementwise max rel err {rel:.3e}")
+    assert rel <= 1e-5

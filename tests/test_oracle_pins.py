@@ -453,3 +453,19 @@ def test_limited_accumulation_reproduces_pages_order_of_magnitude():
     assert target / 4 <= errs[(4096, 11)] * 2 <= target * 4
     assert errs[(16384, 10)] > 2 * errs[(4096, 10)]           # grows with K
     assert errs[(4096, "promoted")] < 1e-6 and errs[(16384, "promoted")] < 1e-6
+
+
+def test_encode_exhaustive_against_torch_cast():
+    """Every non-negative float32 below 464 (1.14e9 bit patterns) and every 61st negative one: the oracle's
+    encoder equals torch's float8_e4m3fn cast (a library routine; it rounds to nearest even and agrees with
+    saturation up to 464, where it turns to NaN)."""
+    top = int(np.array(464.0, np.float32).view(np.uint32))
+    step = 1 << 26
+    for start in range(0, top, step):
+        u = np.arange(start, min(start + step, top), dtype=np.uint32)
+        for bits_ in (u, (u[::61] | np.uint32(0x80000000))):
+            v = bits_.view(np.float32)
+            ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            got = oracle.e4m3_encode_many(v)
+            bad = np.flatnonzero(got != ref)
+            assert bad.size == 0, f"{bad.size} mismatches from {v[bad[0]]!r}: oracle {got[bad[0]]:#x}, torch {ref[bad[0]]:#x}"
