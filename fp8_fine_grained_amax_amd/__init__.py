@@ -44,6 +44,7 @@ def lib():
         L.fg_fp8_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, I, I, P]
         L.fg_amax_bf16.argtypes = [P, I64, I64, I64, P, P]
+        L.fg_fp8_gemm_fprop_limited_accum.argtypes = [P, P, P, P, I64, I64, I64, I, P, P]
         L.fg_quantize_e5m6_1x128.argtypes = [P, I64, I64, I64, P, P, P]
         L.fg_dequantize_e5m6_1x128.argtypes = [P, P, I64, I64, P, I64, P]
         L.fg_requantize_1x128_to_tokens.argtypes = [P, P, I64, I64, I, P, P, P]
@@ -51,7 +52,8 @@ def lib():
         for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop",
                   "fg_fp8_gemm_fprop_quant", "fg_fp8_gemm_dgrad", "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm",
                   "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad", "fg_amax_bf16", "fg_quantize_per_tensor",
-                  "fg_requantize_1x128_to_tokens", "fg_quantize_e5m6_1x128", "fg_dequantize_e5m6_1x128"):
+                  "fg_requantize_1x128_to_tokens", "fg_quantize_e5m6_1x128", "fg_dequantize_e5m6_1x128",
+                  "fg_fp8_gemm_fprop_limited_accum"):
             getattr(L, f).restype = I
         L.fg_status_string.argtypes = [I]
         L.fg_status_string.restype = ctypes.c_char_p
@@ -261,6 +263,19 @@ def fg_fp8_gemm_fprop_quant(xq, sx, wq, sw, yq=None, sy=None, pow2: bool = False
     _check(lib().fg_fp8_gemm_fprop_quant(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(yq), _ptr(sy),
                                          _mode(pow2), _mode(out_pow2), _stream(xq.device)), "fg_fp8_gemm_fprop_quant")
     return yq, sy
+
+
+def fg_fp8_gemm_fprop_limited_accum(xq, sx, wq, sw, mantissa_bits: int, y=None):
+    """Accuracy study: Fprop without FP32 promotion, 32-element matrix-core chunks added to an FP32
+    accumulator truncated to `mantissa_bits` explicit mantissa bits after every addition. fp32 [M, N]."""
+    _gpu(xq, sx, wq, sw, y)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _check(lib().fg_fp8_gemm_fprop_limited_accum(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, int(mantissa_bits),
+                                                 _ptr(y), _stream(xq.device)), "fg_fp8_gemm_fprop_limited_accum")
+    return y
 
 
 def fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.float32, dx=None, pow2: bool = False):

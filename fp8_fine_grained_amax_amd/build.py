@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8fg.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "per_tensor.hip", "e5m6.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "per_tensor.hip", "e5m6.hip", "limited_accum.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

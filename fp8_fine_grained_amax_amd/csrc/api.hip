@@ -38,6 +38,8 @@ hipError_t fg_launch_quant_e5m6(const uint16_t* x, int64_t rows, int64_t cols, i
                                 float* scales, hipStream_t stream);
 hipError_t fg_launch_dequant_e5m6(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols, uint16_t* y,
                                   int64_t ldy, hipStream_t stream);
+hipError_t fg_launch_fprop_limited(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
+                                   int64_t N, int64_t K, int bits, float* y, hipStream_t stream);
 hipError_t fg_launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax, hipStream_t stream);
 hipError_t fg_launch_quant_per_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* hist,
                                       int64_t n_hist, int pow2, int64_t n_scales, uint8_t* q, float* scales,
@@ -92,6 +94,18 @@ fg_status fg_dequantize_e5m6_1x128(const uint8_t* packed, const float* scales, i
     if (!aligned16(y) || (ld_y % 8) != 0 || !aligned4(packed) || !aligned4(scales)) return FG_ERR_MISALIGNED;
     if ((cols / 128) * ((rows + 31) / 32) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_dequant_e5m6(packed, scales, rows, cols, (uint16_t*)y, ld_y, stream));
+}
+
+fg_status fg_fp8_gemm_fprop_limited_accum(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                          int64_t M, int64_t N, int64_t K, int mantissa_bits, float* y,
+                                          hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || mantissa_bits < 1 || mantissa_bits > 23) return FG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return FG_OK;
+    if (!y || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
+    if (K % 128 != 0 || ((M + 15) / 16) * ((N + 15) / 16) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (((uintptr_t)xq & 7u) || ((uintptr_t)wq & 7u) || !aligned4(y) || !aligned4(sx) || !aligned4(sw))
+        return FG_ERR_MISALIGNED;
+    return from_hip(fg_launch_fprop_limited(xq, sx, wq, sw, M, N, K, mantissa_bits, y, stream));
 }
 
 fg_status fg_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax, hipStream_t stream) {

@@ -218,6 +218,19 @@ fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, cons
                                     const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
                                     float* dw, int accumulate, fg_scale_mode scales, hipStream_t stream);
 
+/* ---- Accuracy study: accumulation without promotion ------------------------------------------------
+ * Fprop as fg_fp8_gemm_fprop computes it but WITHOUT the FP32 promotion: every 32-element chunk of the
+ * contraction is one matrix-core partial sum, scaled by its tile and block scales and added to an FP32
+ * accumulator that keeps only `mantissa_bits` explicit mantissa bits (truncated toward zero) after every
+ * addition. It emulates the limited accumulation width that [W1]/[W2] blame for an error of nearly 2% at
+ * K = 4096 (the passage on increasing accumulation precision), for comparison with the promoted GEMMs.
+ * Not part of the training path; written for clarity, not speed.
+ *   xq, sx, wq, sw as for fg_fp8_gemm_fprop; y f32 [M][N].  K % 128 == 0; 1 <= mantissa_bits <= 23
+ *   (23: an ordinary FP32 accumulator). xq, wq 8-byte aligned; y, scales 4-byte aligned. */
+fg_status fg_fp8_gemm_fprop_limited_accum(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
+                                          int64_t M, int64_t N, int64_t K, int mantissa_bits, float* y,
+                                          hipStream_t stream);
+
 /* ---- E5M6 storage of cached activations -------------------------------------------------------------
  * [W1] keeps some cached activations (those entering the Linear after the attention operator) in a
  * customized E5M6 format with power-of-2 scaling factors, and stores forward activations as 1x128 tiles.

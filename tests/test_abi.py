@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -166,3 +166,13 @@ def test_e5m6_rejections(L):
     assert d(A16, None, 4, 128, A16, 128, None) == INVALID              # null scales
     assert d(A16, A16, 4, 128, ODD, 128, None) == MISALIGNED
     assert d(None, None, 0, 128, None, 128, None) == OK
+
+
+def test_limited_accum_rejections(L):
+    f = L.fg_fp8_gemm_fprop_limited_accum
+    assert f(A16, A16, A16, A16, 16, 16, 100, 10, A16, None) == SHAPE        # K % 128
+    assert f(A16, A16, A16, A16, 16, 16, 128, 0, A16, None) == INVALID       # mantissa bits < 1
+    assert f(A16, A16, A16, A16, 16, 16, 128, 24, A16, None) == INVALID      # mantissa bits > 23
+    assert f(A16, A16, None, A16, 16, 16, 128, 10, A16, None) == INVALID     # null W
+    assert f(A16 + 4, A16, A16, A16, 16, 16, 128, 10, A16, None) == MISALIGNED
+    assert f(None, None, None, None, 0, 16, 128, 10, None, None) == OK       # empty

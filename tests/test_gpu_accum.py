@@ -103,3 +103,32 @@ def test_hardware_chain_per_tensor_scale(K):
     rel = np.max(np.abs(y.cpu().numpy().reshape(-1)[pts].astype(np.float64) - exact) / np.abs(exact))
     print(f"\n[accum] K={K} hardware chain, per-tensor power-of-2 scales: elementwise max rel err {rel:.3e}")
     assert rel <= 1e-5
+
+
+def test_gpu_limited_accumulation_matches_oracle_emulation():
+    """The unpromoted accumulation emulated on the GPU (32-element matrix-core chunks into an FP32 register
+    truncated to p mantissa bits) against the oracle's emulation of the same reading: the errors against
+    the exact value agree, reproduce the pages' percent-level error at K = 4096, and grow with K. With
+    p = 23 (a plain FP32 register) the error is small, which also shows the chunk MFMA decodes OCP E4M3."""
+    device()
+    rows = {}
+    for K in (4096, 16384):
+        x, w = wl.accumulation_stress(K)
+        xq, sx = fg.fg_quantize_act_1x128(to_dev(x))
+        wq, sw = fg.fg_quantize_w_128x128(to_dev(w))
+        ops = (np_u8(xq), sx.cpu().numpy(), np_u8(wq), sw.cpu().numpy())
+        pts = sample_points(1024, 1024, 1000, seed=45)
+        _, exact = oracle.gemm_fprop(*ops, pts=pts)
+        for p in (10, 11, 12, 13, 14, 23):
+            y = fg.fg_fp8_gemm_fprop_limited_accum(xq, sx, wq, sw, p)
+            torch.cuda.synchronize()
+            g = np.max(np.abs(y.cpu().numpy().reshape(-1)[pts].astype(np.float64) - exact) / np.abs(exact))
+            o = np.max(np.abs(oracle.gemm_fprop_limited(*ops, chunk=32, bits=p, pts=pts) - exact) / np.abs(exact))
+            rows[(K, p)] = (g, o)
+        print(f"\n[accum] K={K} limited accumulator, GPU vs oracle emulation: " +
+              ", ".join(f"p{p} {rows[(K, p)][0]:.3e}/{rows[(K, p)][1]:.3e}" for p in (10, 11, 12, 13, 14, 23)))
+    for (K, p), (g, o) in rows.items():
+        if p < 23:
+            assert abs(g - o) <= 0.3 * o, (K, p, g, o)
+    assert rows[(4096, 10)][0] > 1e-2 and rows[(16384, 10)][0] > rows[(4096, 10)][0]
+    assert rows[(4096, 23)][0] < 1e-4 and rows[(16384, 23)][0] < 1e-4
