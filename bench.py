@@ -545,6 +545,10 @@ def main():
         "per_tensor_contrast": per_tensor,
         "requantize_tokens": requant,
         "e5m6_storage": e5m6,
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+                   "hip": torch.version.hip, "torch": torch.__version__},
+        "seeds": {"dense_mlp_x_w": 1002, "dense_mlp_dy": 1003, "moe_forward": 1005, "moe_backward": 1006},
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out))
