@@ -327,6 +327,25 @@ def main():
             ms = float(np.median(times))
             gbps = work / (ms * 1e-3) / 1e9
             cold[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        # Reference: plain contiguous device copies moving the same total bytes as the X- and dY-sized
+        # quantizers (3 B per element: 1.5 B read + 1.5 B written here), timed the same cold way: what a
+        # bandwidth-bound kernel of that size reaches on this GPU.
+        for cname, n_el in (("copy_like_quant_x", M * K), ("copy_like_quant_dy", M * N)):
+            src = torch.empty(3 * n_el // 2, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            times = []
+            for _ in range(7):
+                torch.amax(scrub, dim=0, out=sink)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                dst.copy_(src)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            gbps = 3 * n_el / (ms * 1e-3) / 1e9
+            cold[cname] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+            del src, dst
         del scrub
         print("[bench] cold-cache quantize timings done", file=sys.stderr, flush=True)
 
