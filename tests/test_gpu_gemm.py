@@ -421,7 +421,8 @@ def test_grouped_wgrad_moe_share_sampled(pow2):
 @pytest.mark.parametrize("pow2", [False, True])
 def test_tile_shapes_bit_identical(pow2, monkeypatch):
     """Every output element goes through the same instructions in the same order under either workgroup
-    shape, so Fprop, Dgrad, Wgrad and grouped Fprop outputs must match bit for bit (ragged shapes)."""
+    shape, so Fprop (both output types), Dgrad, Wgrad (plain and accumulating) and grouped Fprop outputs
+    must match bit for bit (ragged shapes)."""
     device()
     rng = np.random.default_rng(81)
     M, N, K = 300, 520, 640
@@ -439,13 +440,19 @@ def test_tile_shapes_bit_identical(pow2, monkeypatch):
     xtq, sxt = fg.fg_quantize_act_1x128(xr, axis=fg.FG_ALONG_ROWS, pow2=pow2)
     off = torch.tensor([0, 100, 100, 300], dtype=torch.int32, device=device())
     wg, swg = torch.stack([wq, wq, wq]), torch.stack([sw, sw, sw])
+    dw0 = torch.randn((200, 264), dtype=torch.float32, device=device())
     outs = {}
-    for t in ("256x192", "256x256"):
-        monkeypatch.setenv("FG_GEMM_TILE", t)
-        outs[t] = [fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.float32, pow2=pow2),
-                   fg.fg_fp8_gemm_dgrad(dyq, sdy, wdq, swd, pow2=pow2),
-                   fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, pow2=pow2),
-                   fg.fg_fp8_grouped_gemm(xq, sx, wg, swg, off, out_dtype=torch.float32, pow2=pow2)]
+    for val in ("256x192", "256x256"):
+        monkeypatch.setenv("FG_GEMM_TILE", val)
+        dw_acc = dw0.clone()
+        outs[val] = [fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.float32, pow2=pow2),
+                     fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16, pow2=pow2),
+                     fg.fg_fp8_gemm_dgrad(dyq, sdy, wdq, swd, pow2=pow2),
+                     fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, pow2=pow2),
+                     fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw_acc, accumulate=True, pow2=pow2),
+                     fg.fg_fp8_grouped_gemm(xq, sx, wg, swg, off, out_dtype=torch.float32, pow2=pow2)]
         torch.cuda.synchronize()
-    for name, a, b in zip(("fprop", "dgrad", "wgrad", "grouped"), outs["256x192"], outs["256x256"]):
-        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+    names = ("fprop", "fprop_bf16", "dgrad", "wgrad", "wgrad_accumulate", "grouped")
+    for name, a, b in zip(names, outs["256x192"], outs["256x256"]):
+        assert torch.equal(a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32),
+                           b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32)), name
