@@ -132,6 +132,12 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
     return x * base + (x < extra ? x : extra) + local;
 }
 
+// A device-resident group offset clamped into [lo, hi].
+__device__ __forceinline__ int64_t fg_clamp_offset(int32_t v, int64_t lo, int64_t hi) {
+    const int64_t x = v;
+    return x < lo ? lo : (x > hi ? hi : x);
+}
+
 // E8M0 code of an fp32 power of two in [2^-127, 2^127]: its biased exponent field.
 __device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23) & 0xFF; }
 
@@ -167,7 +173,10 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         // widely, and keeping one group on one XCD would leave that XCD with the longest tiles
         const int g = blockIdx.x / tpg;
         const int local = blockIdx.x % tpg;
-        const int64_t seg0 = p.offsets[g], seg1 = p.offsets[g + 1];
+        // offsets outside [0, T] are clamped into it and a decreasing pair is an empty group, so malformed
+        // offsets give wrong sums but never an access outside the operands
+        const int64_t seg0 = fg_clamp_offset(p.offsets[g], 0, K);
+        const int64_t seg1 = fg_clamp_offset(p.offsets[g + 1], seg0, K);
         const int64_t kb0 = seg0 / BK;
         nkb = (int)((seg1 - seg0) / BK);
         const int mt = local % m_tiles, nt = local / m_tiles;
@@ -195,8 +204,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         int g = 0, cum = 0;
         int64_t seg0 = 0, seg1 = 0;
         for (; g < p.G; g++) {
-            seg0 = p.offsets[g];
-            seg1 = p.offsets[g + 1];
+            // clamped into [0, T] as in the grouped Wgrad: malformed offsets stay inside the operands
+            seg0 = fg_clamp_offset(p.offsets[g], 0, p.M);
+            seg1 = fg_clamp_offset(p.offsets[g + 1], seg0, p.M);
             int mt_g = (int)((seg1 - seg0 + BM - 1) / BM);
             if (id_m < cum + mt_g) break;
             cum += mt_g;

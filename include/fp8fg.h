@@ -189,7 +189,9 @@ fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_
  *   Y[off[g]:off[g+1]][:] = X[off[g]:off[g+1]][:] . W[g]^T
  *   xq u8 [T][K], sx f32 [K/128][T]; wq u8 [G][N][K], sw f32 [G][ceil(N/128)][K/128]; y [T][N].
  *   d_offsets: DEVICE int32 [G+1], non-decreasing, d_offsets[0] == 0, d_offsets[G] == T (precondition,
- *   not re-checked on the host). K % 128 == 0, G >= 1. */
+ *   not re-checked on the host). The kernel clamps each offset into [0, T] and treats a decreasing pair as
+ *   an empty group, so malformed offsets give wrong results but no access outside the operands.
+ *   K % 128 == 0, G >= 1. */
 fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                               const int32_t* d_offsets, int32_t G, int64_t total_rows,
                               int64_t N, int64_t K, void* y, fg_out_dtype out, fg_scale_mode scales,
@@ -201,7 +203,8 @@ fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t*
  *   dyq u8 [T][N], sdy f32 [N/128][T]        (dY quantized FG_ALONG_COLS over all T rows)
  *   wq  u8 [G][N][K], sw f32 [G][N/128][K/128] (the experts' weight codes and blocks, as in Fprop)
  *   dx  [T][K] f32 or bf16.  N % 128 == 0, K % 128 == 0.
- *   d_offsets: DEVICE int32 [G+1] as for fg_fp8_grouped_gemm (precondition, not re-checked). */
+ *   d_offsets: DEVICE int32 [G+1] as for fg_fp8_grouped_gemm (precondition, not re-checked; clamped into
+ *   [0, T] on the device as there). */
 fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
                                     const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
                                     void* dx, fg_out_dtype out, fg_scale_mode scales, hipStream_t stream);
@@ -212,7 +215,8 @@ fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const 
  *   xtq  u8 [K][T], sxt  f32 [T/128][K]   (X quantized FG_ALONG_ROWS)
  *   dw   f32 [G][N][K]; accumulate != 0 starts each element from the value already in dw.
  *   The 1x128 token tiles must not straddle two groups: every d_offsets[g] is a multiple of 128 (a
- *   routed layout padded per expert; precondition, not re-checked). T % 128 == 0, K % 4 == 0.
+ *   routed layout padded per expert; precondition, not re-checked; offsets are clamped into [0, T] on the
+ *   device as for fg_fp8_grouped_gemm). T % 128 == 0, K % 4 == 0.
  *   An empty group writes zeros (or leaves dw unchanged with accumulate). */
 fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
                                     const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,

@@ -418,6 +418,44 @@ def test_grouped_wgrad_moe_share_sampled(pow2):
 # The two workgroup shapes give bit-identical results
 # ------------------------------------------------------------------------------------------------
 
+def test_grouped_offsets_clamped_on_device():
+    """Device offsets outside [0, T] are clamped into it: offsets that start below 0 and end past T give the
+    same outputs, bit for bit, as the offsets they clamp to, and nothing outside the operands is touched."""
+    device()
+    rng = np.random.default_rng(82)
+    T, N, K = 300, 136, 256
+    x = to_dev(_rand_act(rng, T, K))
+    w = to_dev(wl.normal_bf16(rng, (2, N, K), 0.02))
+    xq, sx = fg.fg_quantize_act_1x128(x)
+    wq = torch.stack([fg.fg_quantize_w_128x128(w[g])[0] for g in range(2)])
+    sw = torch.stack([fg.fg_quantize_w_128x128(w[g])[1] for g in range(2)])
+    good = torch.tensor([0, 100, T], dtype=torch.int32, device=device())
+    bad = torch.tensor([-50, 100, T + 1000], dtype=torch.int32, device=device())
+    y_good = fg.fg_fp8_grouped_gemm(xq, sx, wq, sw, good, out_dtype=torch.float32)
+    y_bad = fg.fg_fp8_grouped_gemm(xq, sx, wq, sw, bad, out_dtype=torch.float32)
+    # grouped Dgrad: dY [T, 256] against W [2][256][K]
+    dy = to_dev(_rand_act(rng, T, 256, 1e-3))
+    wd = to_dev(wl.normal_bf16(rng, (2, 256, K), 0.02))
+    dyq, sdy = fg.fg_quantize_act_1x128(dy)
+    wdq = torch.stack([fg.fg_quantize_w_128x128(wd[g])[0] for g in range(2)])
+    swd = torch.stack([fg.fg_quantize_w_128x128(wd[g])[1] for g in range(2)])
+    dx_good = fg.fg_fp8_grouped_gemm_dgrad(dyq, sdy, wdq, swd, good)
+    dx_bad = fg.fg_fp8_grouped_gemm_dgrad(dyq, sdy, wdq, swd, bad)
+    # grouped Wgrad: token segments in multiples of 128
+    Tw = 384
+    dyw = to_dev(_rand_act(rng, Tw, 200, 1e-3))
+    xw = to_dev(_rand_act(rng, Tw, 136))
+    dytq, sdyt = fg.fg_quantize_act_1x128(dyw, axis=fg.FG_ALONG_ROWS)
+    xtq, sxt = fg.fg_quantize_act_1x128(xw, axis=fg.FG_ALONG_ROWS)
+    goodw = torch.tensor([0, 128, Tw], dtype=torch.int32, device=device())
+    badw = torch.tensor([-128, 128, Tw + 256], dtype=torch.int32, device=device())
+    dw_good = fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, goodw)
+    dw_bad = fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, badw)
+    torch.cuda.synchronize()
+    for name, a, b in (("fprop", y_good, y_bad), ("dgrad", dx_good, dx_bad), ("wgrad", dw_good, dw_bad)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+
+
 @pytest.mark.parametrize("pow2", [False, True])
 def test_tile_shapes_bit_identical(pow2, monkeypatch):
     """Every output element goes through the same instructions in the same order under either workgroup
