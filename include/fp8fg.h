@@ -136,7 +136,7 @@ fg_status fg_requantize_1x128_to_tokens(const uint8_t* q_in, const float* s_in, 
  *   w       bf16 [n][k], row stride ld_w; k % 128 == 0; any n >= 0 (a short last block row-group takes
  *           the max over the rows it has).
  *   q       u8 [n][k] (row stride k);  scales f32 [ceil(n/128)][k/128] row-major.
- *   Alignment: w, q 16-byte aligned; ld_w % 8 == 0. */
+ *   Alignment: w, q 16-byte aligned; ld_w % 8 == 0; scales 4-byte aligned. */
 fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_w,
                                 fg_scale_mode mode, uint8_t* q, float* scales, hipStream_t stream);
 
@@ -144,7 +144,7 @@ fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_
  *   xq u8 [M][K], sx f32 [K/128][M]   (from fg_quantize_act_1x128, FG_ALONG_COLS)
  *   wq u8 [N][K], sw f32 [ceil(N/128)][K/128]   (from fg_quantize_w_128x128)
  *   y  [M][N] f32 or bf16 (row stride N).  K % 128 == 0; any M, N >= 0 (M == 0 or N == 0: no-op;
- *   K == 0 writes zeros). Pointers 16-byte aligned. */
+ *   K == 0 writes zeros). xq, wq, y 16-byte aligned; sx, sw 4-byte aligned. */
 fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* y, fg_out_dtype out,
                             fg_scale_mode scales, hipStream_t stream);
@@ -168,7 +168,8 @@ fg_status fg_fp8_gemm_fprop_quant(const uint8_t* xq, const float* sx, const uint
  *   wq  u8 [N][K], sw f32 [N/128][K/128] (the same codes and 128x128 block scales as Fprop; the block
  *       is a 128-group along both axes, so it serves the transposed contraction unchanged; the kernel
  *       reads W transposed on chip, the transposed read the pages ask of future hardware, [W5])
- *   dx  [M][K] f32 or bf16.  N % 128 == 0, K % 128 == 0, any M. */
+ *   dx  [M][K] f32 or bf16.  N % 128 == 0, K % 128 == 0, any M.
+ *   dyq, wq, dx 16-byte aligned; sdy, sw 4-byte aligned. */
 fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* dx, fg_out_dtype out,
                             fg_scale_mode scales, hipStream_t stream);
@@ -179,7 +180,8 @@ fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t*
  *   xtq  u8 [K][M], sxt  f32 [M/128][K]   (X quantized FG_ALONG_ROWS)
  *   dw   f32 [N][K]; weight gradients stay FP32 ([W5], passage on master weights and gradients).
  *        accumulate != 0: the FP32 accumulation of each element starts from the value already in dw.
- *   M % 128 == 0; any N, K >= 0 with K % 4 == 0. */
+ *   M % 128 == 0; any N, K >= 0 with K % 4 == 0. dytq, xtq, dw, sxt 16-byte aligned; sdyt 4-byte
+ *   aligned. */
 fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
                             int64_t M, int64_t N, int64_t K, float* dw, int accumulate,
                             fg_scale_mode scales, hipStream_t stream);
@@ -191,7 +193,7 @@ fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_
  *   d_offsets: DEVICE int32 [G+1], non-decreasing, d_offsets[0] == 0, d_offsets[G] == T (precondition,
  *   not re-checked on the host). The kernel clamps each offset into [0, T] and treats a decreasing pair as
  *   an empty group, so malformed offsets give wrong results but no access outside the operands.
- *   K % 128 == 0, G >= 1. */
+ *   K % 128 == 0, G >= 1. xq, wq, y 16-byte aligned; sx, sw, d_offsets 4-byte aligned. */
 fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                               const int32_t* d_offsets, int32_t G, int64_t total_rows,
                               int64_t N, int64_t K, void* y, fg_out_dtype out, fg_scale_mode scales,
@@ -202,7 +204,8 @@ fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t*
  *   dX[off[g]:off[g+1]][:] = dY[off[g]:off[g+1]][:] . W[g]
  *   dyq u8 [T][N], sdy f32 [N/128][T]        (dY quantized FG_ALONG_COLS over all T rows)
  *   wq  u8 [G][N][K], sw f32 [G][N/128][K/128] (the experts' weight codes and blocks, as in Fprop)
- *   dx  [T][K] f32 or bf16.  N % 128 == 0, K % 128 == 0.
+ *   dx  [T][K] f32 or bf16.  N % 128 == 0, K % 128 == 0. dyq, wq, dx 16-byte aligned; sdy, sw,
+ *   d_offsets 4-byte aligned.
  *   d_offsets: DEVICE int32 [G+1] as for fg_fp8_grouped_gemm (precondition, not re-checked; clamped into
  *   [0, T] on the device as there). */
 fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t* wq, const float* sw,
@@ -216,7 +219,8 @@ fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const 
  *   dw   f32 [G][N][K]; accumulate != 0 starts each element from the value already in dw.
  *   The 1x128 token tiles must not straddle two groups: every d_offsets[g] is a multiple of 128 (a
  *   routed layout padded per expert; precondition, not re-checked; offsets are clamped into [0, T] on the
- *   device as for fg_fp8_grouped_gemm). T % 128 == 0, K % 4 == 0.
+ *   device as for fg_fp8_grouped_gemm). T % 128 == 0, K % 4 == 0. dytq, xtq, dw, sxt 16-byte aligned;
+ *   sdyt, d_offsets 4-byte aligned.
  *   An empty group writes zeros (or leaves dw unchanged with accumulate). */
 fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xtq, const float* sxt,
                                     const int32_t* d_offsets, int32_t G, int64_t total_rows, int64_t N, int64_t K,
