@@ -13,11 +13,11 @@ Also reported, beside the headline: the same step with the other scale mode and 
 launch per tiling ("variants"), per-kernel roofline fractions, cold-cache quantize bandwidth (a 1 GiB
 read between launches defeats the 256 MB Infinity Cache), the Fprop that quantizes its own output
 against Fprop + quantizer, per-tensor (current and delayed) scaling against the 1x128 tiles, the grouped
-MoE GEMMs on one GPU's expert share, the vendor's per-tensor FP8 GEMM at the Fprop shape, and the CPU
-oracle timed on a bounded sample of the workload.
+MoE GEMMs on one GPU's expert share, the tiny and accumulation-stress Fprop shapes, the vendor's
+per-tensor FP8 GEMM at the Fprop shape, and the CPU oracle timed on a bounded sample of the workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pow2] [--no-moe] [--no-cpu] [--no-cold]
-       [--no-vendor] [--no-fused-epilogue] [--no-per-tensor] [--no-overlap] [--calib-copy]
+       [--no-vendor] [--no-fused-epilogue] [--no-per-tensor] [--no-small] [--no-overlap] [--calib-copy]
 
 The headline uses fp32 scales (amax/448); --pow2 makes power-of-2 scales the headline.
 """
@@ -70,6 +70,7 @@ def main():
     ap.add_argument("--no-vendor", action="store_true")
     ap.add_argument("--no-fused-epilogue", action="store_true")
     ap.add_argument("--no-per-tensor", action="store_true")
+    ap.add_argument("--no-small", action="store_true", help="skip the tiny and accumulation-stress timings")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the two-stream schedule (a profile's per-kernel means then hold sequential launches only)")
     ap.add_argument("--pow2", action="store_true", help="power-of-2 scales (quantizers round scales up to 2^k; "
@@ -353,6 +354,53 @@ def main():
         del scrub
         print("[bench] cold-cache quantize timings done", file=sys.stderr, flush=True)
 
+    # The small configurations (parity cases, timed for completeness): the tiny Fprop X [128,512] . W [256,512]^T
+    # and the accumulation-stress Fprop X [1024,K] . W [1024,K]^T, K = 4096 and 16384, fp32 scales, FP32 out.
+    # Each launch is event-timed alone (5 untimed launches, then the median and minimum of 20); at these
+    # sizes the kernels are launch-bound, so the fractions of peak are small by construction.
+    small = None
+    if not args.no_small:
+        def event_ms(fn, warm=5, iters=20):
+            for _ in range(warm):
+                fn()
+            ts = []
+            for _ in range(iters):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts)), float(np.min(ts))
+
+        small = {}
+        cases = [("tiny_fprop_128x256x512", wl.tiny_fprop())]
+        cases += [(f"accumulation_stress_1024x1024x{k}", wl.accumulation_stress(k)) for k in (4096, 16384)]
+        for cname, (xs, ws) in cases:
+            xd, wd = xs.to(dev), ws.to(dev)
+            mm, nn, kk = xd.shape[0], wd.shape[0], xd.shape[1]
+            xq_s, sx_s = fg.fg_quantize_act_1x128(xd)
+            wq_s, sw_s = fg.fg_quantize_w_128x128(wd)
+            y_s = torch.empty((mm, nn), dtype=torch.float32, device=dev)
+            entry = {}
+            for kname, fn, work, bound in (
+                    ("quant_x_rowwise", lambda: fg.fg_quantize_act_1x128(xd, q=xq_s, scales=sx_s), quant_bytes(mm, kk), "hbm"),
+                    ("quant_w_128x128", lambda: fg.fg_quantize_w_128x128(wd, q=wq_s, scales=sw_s), quant_w_bytes(nn, kk), "hbm"),
+                    ("fprop_f32", lambda: fg.fg_fp8_gemm_fprop(xq_s, sx_s, wq_s, sw_s, out_dtype=torch.float32, y=y_s),
+                     2.0 * mm * nn * kk, "mfma")):
+                med, mn = event_ms(fn)
+                if bound == "hbm":
+                    rate = work / (med * 1e-3) / 1e9
+                    entry[kname] = {"us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2), "GB/s": round(rate, 1),
+                                    "frac_hbm_peak": round(rate / PEAK_HBM_GBPS, 4)}
+                else:
+                    rate = work / (med * 1e-3) / 1e12
+                    entry[kname] = {"us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2), "TFLOP/s": round(rate, 2),
+                                    "frac_fp8_peak": round(rate / PEAK_FP8_TFLOPS, 4)}
+            small[cname] = entry
+            del xd, wd, xq_s, sx_s, wq_s, sw_s, y_s
+        print("[bench] small-configuration timings done", file=sys.stderr, flush=True)
+
     # Fprop whose BF16 output is wanted as 1x128 FP8 tiles (the next layer's input): the GEMM writing BF16
     # and a quantizer reading it back, against the GEMM quantizing in its epilogue (same codes and scales).
     fused_epi = None
@@ -563,6 +611,7 @@ def main():
                          "kernel_ms": {n: round(v, 4) for n, v in vper.items()}}
                      for k, (vops, vms, vper) in variants.items()},
         "quantize_cold_cache": cold,
+        "small_configs": small,
         "vendor_fp8_gemm_reference": vendor,
         "moe_grouped": moe,
         "fprop_output_quantized": fused_epi,
