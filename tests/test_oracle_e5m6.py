@@ -94,3 +94,38 @@ def test_dequantize_rounds_bf16_to_seven_significant_bits():
     normal = np.abs(oracle.bf16_bits_to_f32(xb)) >= 2.0 ** -14 * np.repeat(s.T, 128, axis=1)
     assert normal.mean() > 0.99
     assert np.array_equal(y[normal], expected[normal])
+
+
+def _golden(kind):
+    path = __file__.rsplit("/", 1)[0] + "/golden/e5m6_worked_examples.txt"
+    for line in open(path):
+        if line.startswith(kind + " |"):
+            yield [f.strip() for f in line.split("|")[1:]]
+
+
+def test_golden_worked_codes():
+    """Hand-derived codes (tests/golden/e5m6_worked_examples.txt): normal, subnormal, saturated values and
+    exact ties to the even code, through both the encoder and the decoder."""
+    rows = list(_golden("code"))
+    assert len(rows) == 13
+    vals = np.array([float(v) for v, _ in rows], np.float32)
+    want = np.array([int(c, 16) for _, c in rows], np.uint16)
+    assert np.array_equal(oracle.e5m6_encode(vals), want)
+    dec = oracle.e5m6_decode(want)
+    assert dec[0] == 1.0 and dec[1] == -3.0 and dec[2] == 0.099609375 and dec[3] == 65024.0
+
+
+def test_golden_worked_tile():
+    """A hand-derived 1x128 tile: its power-of-2 scale, its codes and their three-bytes-per-two packing."""
+    (vals, scale, codes, packed), = list(_golden("tile"))
+    x = np.zeros((1, 128), np.float32)
+    v = [float(t) for t in vals.split()]
+    x[0, :len(v)] = v
+    xb = wl.bf16_bits(wl.to_bf16(x))
+    p, s = oracle.quantize_e5m6_1x128(xb)
+    assert s[0, 0] == np.float32(float(scale))
+    c = [int(t, 16) for t in codes.split()]
+    assert np.array_equal(oracle.e5m6_unpack(p)[0, :len(c)], np.array(c, np.uint16))
+    b = [int(t, 16) for t in packed.split()]
+    assert np.array_equal(p[0, :len(b)], np.array(b, np.uint8))
+    assert np.array_equal(oracle.dequantize_e5m6_1x128(p, s)[0, :3], xb[0, :3])
