@@ -585,7 +585,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(kernels)
 
     qnames = [n for n, _, b, _ in ops if b == "hbm"]
     qbytes = sum(wk for n, _, b, wk in ops if b == "hbm")
@@ -656,41 +656,97 @@ def vendor_reference(M, N, K, dev):
         return {"error": repr(ex)[:200]}
 
 
-def cpu_baseline():
-    """The oracle as it stands, on a bounded sample of the step's GEMM work (sampled Fprop outputs at the
-    full shape, each a full 128-blocked promoted dot product), run for ~10-20 s on the host's cores.
-    Reported in the same unit as `value`, with the thread count and the CPU model."""
+def cpu_baseline(gpu_kernels=None, budget_s=24.0):
+    """The oracle as it stands, timed beside each GPU kernel of the step on the host's cores (OpenMP over
+    all of them, within about `budget_s` seconds of CPU work in total):
+      - the quantizers on the full tensors of the step (X both tilings, W 128x128 blocks, dY both tilings;
+        the oracle has no fused kernel, so "both tilings" is its two single-tiling passes), in GB/s of the
+        same algorithmic bytes the GPU rate uses;
+      - Fprop, Dgrad and Wgrad on sampled outputs of the full-size GEMMs (each sample a full-depth promoted
+        dot product), in TFLOP/s.
+    `value` is the oracle's GEMM rate over the three sampled GEMMs together, in the unit of the headline;
+    per_op gives each op's rate, the GPU kernel's rate from the same run, and their ratio."""
     import numpy as np
     import oracle
     from fp8_fine_grained_amax_amd import workloads as wl
 
     shape = wl.DSV3_MLP
     M, N, K = shape.M, shape.N, shape.K
-    rng = np.random.default_rng(99)
-    # codes and scales with the workload's value ranges (the oracle's GEMM cost does not depend on them)
-    xq = rng.integers(0, 0x7E, (M, K), dtype=np.uint8)
-    wq = rng.integers(0, 0x7E, (N, K), dtype=np.uint8)
-    sx = rng.uniform(1e-3, 1e-2, (K // 128, M)).astype(np.float32)
-    sw = rng.uniform(1e-5, 1e-4, (N // 128, K // 128)).astype(np.float32)
-    npts, total_flop, elapsed = 256, 0.0, 0.0
-    while elapsed < 10.0 and npts <= 1 << 22:
-        pts = rng.integers(0, M * N, npts, dtype=np.int64)
+    per_op = {}
+    t_start = time.perf_counter()
+
+    def timed(fn):
         t = time.perf_counter()
-        oracle.gemm_fprop(xq, sx, wq, sw, out_bf16=True, pts=pts, want_exact=False)
-        dt = time.perf_counter() - t
-        elapsed += dt
-        total_flop += 2.0 * K * npts
-        npts *= 2
-    value = total_flop / elapsed / 1e12
+        fn()
+        return time.perf_counter() - t
+
+    # quantizers: the step's own bf16 inputs
+    x, w = wl.dsv3_fprop()
+    dy = wl.dsv3_backward_dy()
+    xb, wb, dyb = wl.bf16_bits(x), wl.bf16_bits(w), wl.bf16_bits(dy)
+    del x, w, dy
+    for name, fn, nbytes in (
+            ("quant_x_both", lambda: (oracle.quantize_act_1x128(xb, 0, False), oracle.quantize_act_1x128(xb, 1, False)),
+             quant_both_bytes(M, K)),
+            ("quant_w_128x128", lambda: oracle.quantize_w_128x128(wb, False), quant_w_bytes(N, K)),
+            ("quant_dy_both", lambda: (oracle.quantize_act_1x128(dyb, 0, False), oracle.quantize_act_1x128(dyb, 1, False)),
+             quant_both_bytes(M, N))):
+        dt = timed(fn)
+        per_op[name] = {"oracle_GB/s": round(nbytes / dt / 1e9, 3), "oracle_s": round(dt, 3),
+                        "sample": "the full tensor"}
+    del xb, wb, dyb
+
+    # GEMMs: codes and scales with the workload's value ranges (the oracle's cost does not depend on them)
+    rng = np.random.default_rng(99)
+    a_mk = rng.integers(0, 0x7E, (M, K), dtype=np.uint8)
+    b_nk = rng.integers(0, 0x7E, (N, K), dtype=np.uint8)
+    s_km = rng.uniform(1e-3, 1e-2, (K // 128, M)).astype(np.float32)
+    s_blk = rng.uniform(1e-5, 1e-4, (N // 128, K // 128)).astype(np.float32)
+    a_mn = rng.integers(0, 0x7E, (M, N), dtype=np.uint8)
+    s_nm = rng.uniform(1e-3, 1e-2, (N // 128, M)).astype(np.float32)
+    at_nm = rng.integers(0, 0x7E, (N, M), dtype=np.uint8)
+    at_km = rng.integers(0, 0x7E, (K, M), dtype=np.uint8)
+    s_mn = rng.uniform(1e-3, 1e-2, (M // 128, N)).astype(np.float32)
+    s_mk = rng.uniform(1e-3, 1e-2, (M // 128, K)).astype(np.float32)
+    gemms = (("fprop", M * N, K, lambda p: oracle.gemm_fprop(a_mk, s_km, b_nk, s_blk, out_bf16=True, pts=p,
+                                                               want_exact=False)),
+             ("dgrad", M * K, N, lambda p: oracle.gemm_dgrad(a_mn, s_nm, b_nk, s_blk, pts=p, want_exact=False)),
+             ("wgrad", N * K, M, lambda p: oracle.gemm_wgrad(at_nm, s_mn, at_km, s_mk, pts=p, want_exact=False)))
+    left = max(budget_s - (time.perf_counter() - t_start), 6.0)
+    total_flop, total_s = 0.0, 0.0
+    for name, n_out, depth, fn in gemms:
+        npts, flop, el = 256, 0.0, 0.0
+        while el < left / 3 and npts <= 1 << 22:
+            pts = rng.integers(0, n_out, npts, dtype=np.int64)
+            el += timed(lambda: fn(pts))
+            flop += 2.0 * depth * npts
+            npts *= 2
+        per_op[name] = {"oracle_TFLOP/s": round(flop / el / 1e12, 6), "oracle_s": round(el, 2),
+                        "sample": f"{int(flop / (2 * depth))} sampled outputs, each a {depth}-deep promoted dot product"}
+        total_flop += flop
+        total_s += el
+    if gpu_kernels:
+        for name, entry in per_op.items():
+            g = gpu_kernels.get(name)
+            if not g:
+                continue
+            if "TFLOP/s" in g:
+                entry["gpu_TFLOP/s"] = g["TFLOP/s"]
+                entry["gpu_over_oracle"] = round(g["TFLOP/s"] / entry["oracle_TFLOP/s"], 1)
+            elif "GB/s" in g:
+                entry["gpu_GB/s"] = g["GB/s"]
+                entry["gpu_over_oracle"] = round(g["GB/s"] / entry["oracle_GB/s"], 1)
     model = None
     try:
         with open("/proc/cpuinfo") as f:
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "cpu_model": model, "kind": "oracle",
-            "sample": f"{int(total_flop / (2 * K))} sampled Fprop outputs of the 4096x18432x7168 GEMM "
-                      f"(each a 7168-deep promoted dot product), {elapsed:.1f} s"}
+    return {"value": total_flop / total_s / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "cpu_model": model,
+            "kind": "oracle",
+            "sample": f"sampled outputs of the step's three 4096x18432x7168 GEMMs ({total_s:.1f} s), plus the "
+                      f"step's quantizers on their full tensors (per_op)",
+            "per_op": per_op}
 
 
 if __name__ == "__main__":

@@ -40,6 +40,13 @@ def build(verbose: bool = False, extra=()) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # The library must load with every symbol resolved: a kernel missing from the host object (its launch
+    # stub not emitted) shows up only here, as an undefined symbol.
+    r = subprocess.run([sys.executable, "-c", "import ctypes, sys; ctypes.CDLL(sys.argv[1], mode=ctypes.RTLD_LOCAL)",
+                        LIB + ".tmp"], capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr + "\n")
+        raise RuntimeError("the built library does not load: " + r.stderr.strip().splitlines()[-1])
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -55,6 +55,11 @@ constexpr int64_t kMaxGridY = 65535LL;
 constexpr int64_t kMaxGemmTiles = 2147483647LL;
 constexpr int32_t kMaxGroups = 65536;
 constexpr int64_t kMaxFlatChunks = 1LL << 31;   // per-tensor kernels index 16 B chunks in 32 bits
+// The GEMM kernels address a tile's operand rows with 32-bit offsets from the tile base: up to 255 rows of
+// the contraction length (A, and B stored [N][K]), and up to 128 rows of the output width for the
+// transposed B of Dgrad. These bounds keep every such offset below 2^32.
+constexpr int64_t kMaxContraction = 1LL << 24;
+constexpr int64_t kMaxTransposedWidth = 1LL << 25;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -68,7 +73,11 @@ fg_status from_hip(hipError_t e) {
 bool valid_mode(int m) { return m == FG_SCALE_FP32 || m == FG_SCALE_POW2; }
 bool valid_out(int o) { return o == FG_OUT_F32 || o == FG_OUT_BF16; }
 
-int64_t tiles(int64_t a, int64_t b) { return ((a + 255) / 256) * ((b + 127) / 128); }
+// Size arithmetic on caller-supplied extents, free of signed overflow for any non-negative input.
+int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0); }        // ceil(a / b), a >= 0, b > 0
+bool prod_over(int64_t a, int64_t b, int64_t limit) { return a != 0 && b > limit / a; }   // a * b > limit
+// Output tiles of a GEMM counted at the finest tile any launch uses (256 x 128): more than the grid holds?
+bool too_many_tiles(int64_t a, int64_t b) { return prod_over(cdiv(a, 256), cdiv(b, 128), kMaxGemmTiles); }
 
 }  // namespace
 
@@ -81,7 +90,7 @@ fg_status fg_quantize_e5m6_1x128(const void* x, int64_t rows, int64_t cols, int6
     if (!x || !packed || !scales) return FG_ERR_INVALID_ARG;
     if (cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(x) || (ld_x % 8) != 0 || !aligned4(packed) || !aligned4(scales)) return FG_ERR_MISALIGNED;
-    if ((cols / 128) * ((rows + 31) / 32) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (prod_over(cols / 128, cdiv(rows, 32), kMaxGridX)) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_quant_e5m6((const uint16_t*)x, rows, cols, ld_x, packed, scales, stream));
 }
 
@@ -92,7 +101,7 @@ fg_status fg_dequantize_e5m6_1x128(const uint8_t* packed, const float* scales, i
     if (!packed || !scales || !y) return FG_ERR_INVALID_ARG;
     if (cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(y) || (ld_y % 8) != 0 || !aligned4(packed) || !aligned4(scales)) return FG_ERR_MISALIGNED;
-    if ((cols / 128) * ((rows + 31) / 32) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (prod_over(cols / 128, cdiv(rows, 32), kMaxGridX)) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_dequant_e5m6(packed, scales, rows, cols, (uint16_t*)y, ld_y, stream));
 }
 
@@ -102,7 +111,7 @@ fg_status fg_fp8_gemm_fprop_limited_accum(const uint8_t* xq, const float* sx, co
     if (M < 0 || N < 0 || K < 0 || mantissa_bits < 1 || mantissa_bits > 23) return FG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return FG_OK;
     if (!y || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
-    if (K % 128 != 0 || ((M + 15) / 16) * ((N + 15) / 16) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (K % 128 != 0 || prod_over(cdiv(M, 16), cdiv(N, 16), kMaxGridX)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (((uintptr_t)xq & 7u) || ((uintptr_t)wq & 7u) || !aligned4(y) || !aligned4(sx) || !aligned4(sw))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_fprop_limited(xq, sx, wq, sw, M, N, K, mantissa_bits, y, stream));
@@ -112,7 +121,7 @@ fg_status fg_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t ld_x, 
     if (rows < 0 || cols < 0 || ld_x < cols) return FG_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return FG_OK;
     if (!x || !amax) return FG_ERR_INVALID_ARG;
-    if (cols % 8 != 0 || rows * (cols / 8) >= kMaxFlatChunks) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (cols % 8 != 0 || prod_over(rows, cols / 8, kMaxFlatChunks - 1)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(x) || !aligned4(amax) || (ld_x % 8) != 0) return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_amax((const uint16_t*)x, rows, cols, ld_x, amax, stream));
 }
@@ -126,7 +135,7 @@ fg_status fg_quantize_per_tensor(const void* x, int64_t rows, int64_t cols, int6
     if (rows == 0) return FG_OK;
     if (!x || !q || !scales || (n_hist > 0 && !amax_hist)) return FG_ERR_INVALID_ARG;
     if (amax_out && n_hist > 0 && amax_out >= amax_hist && amax_out < amax_hist + n_hist) return FG_ERR_INVALID_ARG;
-    if (cols % 128 != 0 || n_hist > 4096 || rows * (cols / 8) >= kMaxFlatChunks) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (cols % 128 != 0 || n_hist > 4096 || prod_over(rows, cols / 8, kMaxFlatChunks - 1)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (cols == 0) return FG_OK;
     if (!aligned16(x) || !aligned16(q) || (ld_x % 8) != 0 || !aligned4(scales) || (amax_hist && !aligned4(amax_hist)) ||
         (amax_out && !aligned4(amax_out)))
@@ -160,11 +169,11 @@ fg_status fg_quantize_act_1x128(const void* x, int64_t rows, int64_t cols, int64
     const int pow2 = mode == FG_SCALE_POW2;
     if (axis == FG_ALONG_COLS) {
         if (cols % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-        if ((cols / 128) * ((rows + 31) / 32) > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+        if (prod_over(cols / 128, cdiv(rows, 32), kMaxGridX)) return FG_ERR_UNSUPPORTED_SHAPE;
         return from_hip(fg_launch_quant_act_cols((const uint16_t*)x, rows, cols, ld_x, pow2, q, scales, stream));
     }
     if (rows % 128 != 0 || cols % 8 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-    if ((cols + 63) / 64 > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (cdiv(cols, 64) > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_quant_act_rows((const uint16_t*)x, rows, cols, ld_x, pow2, q, scales, stream));
 }
 
@@ -201,7 +210,7 @@ fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_
     if (!w || !q || !scales) return FG_ERR_INVALID_ARG;
     if (k % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(w) || !aligned16(q) || !aligned4(scales) || (ld_w % 8) != 0) return FG_ERR_MISALIGNED;
-    if ((n + 127) / 128 > kMaxGridY || k / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (cdiv(n, 128) > kMaxGridY || k / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_quant_w((const uint16_t*)w, n, k, ld_w, mode == FG_SCALE_POW2, q, scales, stream));
 }
 
@@ -210,7 +219,7 @@ fg_status fg_fp8_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* w
     if (M < 0 || N < 0 || K < 0 || !valid_out(out) || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return FG_OK;
     if (!y || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
-    if (K % 128 != 0 || tiles(M, N) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (K % 128 != 0 || K > kMaxContraction || too_many_tiles(M, N)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw)) return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_fprop(xq, sx, wq, sw, M, N, K, y, out == FG_OUT_BF16, scales == FG_SCALE_POW2, stream));
 }
@@ -221,7 +230,8 @@ fg_status fg_fp8_gemm_fprop_quant(const uint8_t* xq, const float* sx, const uint
     if (M < 0 || N < 0 || K < 0 || !valid_mode(scales) || !valid_mode(out_scales)) return FG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return FG_OK;
     if (!yq || !sy || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
-    if (N % 128 != 0 || K % 128 != 0 || tiles(M, N) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (N % 128 != 0 || K % 128 != 0 || K > kMaxContraction || too_many_tiles(M, N))
+        return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(yq) || !aligned4(sx) || !aligned4(sw) || !aligned4(sy))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_fprop_quant(xq, sx, wq, sw, M, N, K, yq, sy, scales == FG_SCALE_POW2,
@@ -233,7 +243,8 @@ fg_status fg_fp8_gemm_dgrad(const uint8_t* dyq, const float* sdy, const uint8_t*
     if (M < 0 || N < 0 || K < 0 || !valid_out(out) || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
     if (M == 0 || K == 0) return FG_OK;
     if (!dx || (N > 0 && (!dyq || !sdy || !wq || !sw))) return FG_ERR_INVALID_ARG;
-    if (N % 128 != 0 || K % 128 != 0 || tiles(M, K) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction || K > kMaxTransposedWidth || too_many_tiles(M, K))
+        return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(dyq) || !aligned16(wq) || !aligned16(dx) || !aligned4(sdy) || !aligned4(sw)) return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_dgrad(dyq, sdy, wq, sw, M, N, K, dx, out == FG_OUT_BF16, scales == FG_SCALE_POW2, stream));
 }
@@ -243,7 +254,7 @@ fg_status fg_fp8_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_
     if (M < 0 || N < 0 || K < 0 || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
     if (N == 0 || K == 0) return FG_OK;
     if (!dw || (M > 0 && (!dytq || !sdyt || !xtq || !sxt))) return FG_ERR_INVALID_ARG;
-    if (M % 128 != 0 || K % 4 != 0 || tiles(N, K) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (M % 128 != 0 || K % 4 != 0 || M > kMaxContraction || too_many_tiles(N, K)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(dytq) || !aligned16(xtq) || !aligned16(dw) || !aligned16(sxt) || !aligned4(sdyt))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_wgrad(dytq, sdyt, xtq, sxt, M, N, K, dw, accumulate != 0, scales == FG_SCALE_POW2, stream));
@@ -256,8 +267,8 @@ fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t*
         return FG_ERR_INVALID_ARG;
     if (total_rows == 0 || N == 0) return FG_OK;
     if (!y || !d_offsets || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
-    if (K % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-    if (((total_rows + 255) / 256 + G) * ((N + 127) / 128) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (K % 128 != 0 || K > kMaxContraction) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (prod_over(cdiv(total_rows, 256) + G, cdiv(N, 128), kMaxGemmTiles)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw) || !aligned4(d_offsets))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_grouped(xq, sx, wq, sw, d_offsets, G, total_rows, N, K, y, out == FG_OUT_BF16,
@@ -271,8 +282,8 @@ fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const 
         return FG_ERR_INVALID_ARG;
     if (total_rows == 0 || K == 0) return FG_OK;
     if (!dx || !d_offsets || (N > 0 && (!dyq || !sdy || !wq || !sw))) return FG_ERR_INVALID_ARG;
-    if (N % 128 != 0 || K % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-    if (((total_rows + 255) / 256 + G) * ((K + 127) / 128) > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction || K > kMaxTransposedWidth) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (prod_over(cdiv(total_rows, 256) + G, cdiv(K, 128), kMaxGemmTiles)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(dyq) || !aligned16(wq) || !aligned16(dx) || !aligned4(sdy) || !aligned4(sw) || !aligned4(d_offsets))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_grouped_dgrad(dyq, sdy, wq, sw, d_offsets, G, total_rows, N, K, dx, out == FG_OUT_BF16,
@@ -285,8 +296,9 @@ fg_status fg_fp8_grouped_gemm_wgrad(const uint8_t* dytq, const float* sdyt, cons
     if (G < 1 || G > kMaxGroups || total_rows < 0 || N < 0 || K < 0 || !valid_mode(scales)) return FG_ERR_INVALID_ARG;
     if (N == 0 || K == 0) return FG_OK;
     if (!dw || !d_offsets || (total_rows > 0 && (!dytq || !sdyt || !xtq || !sxt))) return FG_ERR_INVALID_ARG;
-    if (total_rows % 128 != 0 || K % 4 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
-    if (tiles(N, K) * G > kMaxGemmTiles) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (total_rows % 128 != 0 || K % 4 != 0 || total_rows > kMaxContraction) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (too_many_tiles(N, K) || prod_over(cdiv(N, 256) * cdiv(K, 128), G, kMaxGemmTiles))
+        return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(dytq) || !aligned16(xtq) || !aligned16(dw) || !aligned16(sxt) || !aligned4(sdyt) ||
         !aligned4(d_offsets))
         return FG_ERR_MISALIGNED;

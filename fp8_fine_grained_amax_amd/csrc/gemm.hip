@@ -132,14 +132,44 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
     return x * base + (x < extra ? x : extra) + local;
 }
 
+#ifndef FG_BUFFER_LOADS
+#define FG_BUFFER_LOADS 1
+#endif
+// Raw buffer descriptor over [base, base + 2^32 - 1): stride 0, no swizzle; the range check never
+// triggers for the 32-bit offsets the kernels use (the host bounds the sizes so they stay below 2^32).
+// The base is wave-uniform by construction; taking it through readfirstlane states so, and the descriptor
+// then lives in SGPRs without a per-lane loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fg_buffer_rsrc(const void* base) {
+    const uint64_t u = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    void* b = (void*)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+}
+
+// 16-byte direct-to-LDS buffer load (lane l lands at byte 16 l of the LDS destination). The call is
+// compiled in the device pass only: the host pass checks this builtin's size operand against its own
+// target, rejects 16 without a diagnostic and then drops every kernel that uses it from the host object.
+__device__ __forceinline__ void fg_buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FG_LDS(lds), 16, voffset, 0, 0, 0);
+#endif
+}
+
 // A device-resident group offset clamped into [lo, hi].
 __device__ __forceinline__ int64_t fg_clamp_offset(int32_t v, int64_t lo, int64_t hi) {
     const int64_t x = v;
     return x < lo ? lo : (x > hi ? hi : x);
 }
 
-// E8M0 code of an fp32 power of two in [2^-127, 2^127]: its biased exponent field.
-__device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23) & 0xFF; }
+// E8M0 code of an fp32 power of two in [2^-126, 2^127]: its biased exponent field. `bad` collects the bits
+// that a power-of-two scale never has (sign and mantissa), so a power-of-2 launch handed other scales can
+// poison its outputs instead of silently dropping the mantissas.
+__device__ __forceinline__ int e8m0_of(float s, uint32_t& bad) {
+    const uint32_t u = __float_as_uint(s);
+    bad |= u & 0x807FFFFFu;
+    return (int)(u >> 23) & 0xFF;
+}
 
 template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE>
 __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
@@ -319,6 +349,27 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
 
     // Load q of the wave's LOADS_PER_WAVE for K step kb into stage st: A instructions, then B, then the
     // scale slice. `issue_piece(kb, st, i)` issues the i-th of MSUB near-equal pieces of that sequence.
+#if FG_BUFFER_LOADS
+    // Buffer-descriptor form of the direct-to-LDS loads: a wave-uniform base (rebuilt per K step in SGPRs)
+    // plus the lane's 32-bit offset. Unlike the global form, which the compiler must treat as a pending
+    // LDS access of unknown order, it leaves the LDS fragment reads countable one by one, so a wait for
+    // one fragment does not also wait for the fragments read ahead of it.
+    const uint32_t sc_off = (uint32_t)(sc_row * 4);
+    auto issue_load = [&](int kb, int st, int q) {
+        if (q < C::UA) {
+            const auto rs = fg_buffer_rsrc(a_tile + (int64_t)kb * BK);
+            fg_buffer_load_lds16(rs, stA(st) + a_t[q] * 1024, a_off[q]);
+        } else if (q < C::UA + C::UB) {
+            const int u = q - C::UA;
+            const auto rs = fg_buffer_rsrc(B_TRANS ? b_tile + (int64_t)kb * BK * N : b_tile + (int64_t)kb * BK);
+            fg_buffer_load_lds16(rs, stB(st) + b_t[u] * 1024, b_off[u]);
+        } else {
+            const auto rs = fg_buffer_rsrc(sc_is_b ? SBp + (int64_t)kb * N : SAp + (int64_t)kb * p.sa_ld);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FG_LDS(reinterpret_cast<uint8_t*>(stSA(st)) + sc_dst), 4, sc_off,
+                                                     0, 0, 0);
+        }
+    };
+#else
     auto issue_load = [&](int kb, int st, int q) {
         if (q < C::UA) {
             const uint8_t* a_k = a_tile + (int64_t)kb * BK;
@@ -333,6 +384,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                                              0, 0);
         }
     };
+#endif
     // Pieces go out ahead of the first F MFMA rows of the step (loads issued early have longer to land;
     // loads spread out disturb the MFMA stream less). Measured per shape on the dense-MLP GEMMs:
     // 256x192: F = 2; 256x256 with 128x128 weight blocks (Fprop, Dgrad): F = 3; per-row B scales (Wgrad):
@@ -411,6 +463,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     // The 128x128 block scale of step kb+1 is fetched with that step's tile loads, so the wait at the top
     // of each step covers it and no step waits on a scale load of its own.
     float sb_next = 1.0f;
+    uint32_t bad_scale = 0;                 // power-of-2 mode: sign or mantissa bits seen in any scale
     if (nkb > 0) {
 #pragma unroll
         for (int q = 0; q < C::LOADS_PER_WAVE; q++) issue_load(0, 0, q);
@@ -428,6 +481,13 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         const uint8_t* sAs = stA(st);
         const uint8_t* sBs = stB(st);
         const float* sSA = stSA(st);
+        const uint8_t* sA_w = sAs + wm * WAVE_M * BK;
+        const float* sSA_w = sSA + wm * WAVE_M + lrow;
+        // A-role fragments are read one row of tiles ahead (two register sets): the first row's is read
+        // before the B fragments, so the step's first MFMA waits only for the reads it needs, and every
+        // later row's read has the previous row's MFMAs to land behind.
+        v8i af_next = frag_at(sA_w, frag_lo, frag_hi);
+        float sa_next = sSA_w[0];
         // B-role fragments for the wave's NSUB N tiles, held for the whole K step
         v8i bf[NSUB];
 #pragma unroll
@@ -444,8 +504,25 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                 bf[j] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
             }
         }
-        const uint8_t* sA_w = sAs + wm * WAVE_M * BK;
-        const float* sSA_w = sSA + wm * WAVE_M + lrow;
+        // Two A register sets fit wherever the promotion leaves 8 registers free; the FP32-scale Wgrad
+        // (per-row B scales) and the 256x256 FP32-scale Fprop read each row's fragment just before it.
+        constexpr bool AF_AHEAD = POW2 || SBK == SB_BLOCK_T || (C::NW == 12 && SBK == SB_BLOCK);
+        // Row i's A fragment and A-row scale (the scale is read with the fragment, so waiting for one
+        // never waits for reads issued after it).
+        auto next_af = [&](int i, float& sa) -> v8i {
+            if constexpr (AF_AHEAD) {
+                const v8i af = af_next;
+                sa = sa_next;
+                if (i + 1 < MSUB) {
+                    af_next = frag_at(sA_w + (i + 1) * 16 * BK, frag_lo, frag_hi);
+                    sa_next = sSA_w[(i + 1) * 16];
+                }
+                return af;
+            } else {
+                sa = i == 0 ? sa_next : sSA_w[i * 16];
+                return i == 0 ? af_next : frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
+            }
+        };
         if constexpr (POW2) {
             // Power-of-two scales: the matrix core applies them itself. Per lane l the E8M0 scale operand
             // of a 16x128 fragment scales row l%16 (all four 32-element K sub-blocks of the lane carry the
@@ -455,12 +532,14 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
             int eb[NSUB];
 #pragma unroll
             for (int j = 0; j < NSUB; j++)
-                eb[j] = SBK == SB_ROW ? e8m0_of(stSB(st)[wn * WAVE_N + j * 16 + lrow]) : e8m0_of(sb_blk);
+                eb[j] = SBK == SB_ROW ? e8m0_of(stSB(st)[wn * WAVE_N + j * 16 + lrow], bad_scale)
+                                      : e8m0_of(sb_blk, bad_scale);
 #pragma unroll
             for (int i = 0; i < MSUB; i++) {
                 issue_piece(kb1, st ^ 1, i);
-                const v8i af = frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
-                const int ea = e8m0_of(sSA_w[i * 16]);
+                float sa_i;
+                const v8i af = next_af(i, sa_i);
+                const int ea = e8m0_of(sa_i, bad_scale);
                 if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(MFMA_PRIO);
 #pragma unroll
                 for (int j = 0; j < NSUB; j++)
@@ -489,8 +568,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                     float sa_i = 0.f;
                     if (i < MSUB) {
                         issue_piece(kb1, st ^ 1, i);
-                        const v8i af = frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
-                        sa_i = sSA_w[i * 16];
+                        const v8i af = next_af(i, sa_i);
                         if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(MFMA_PRIO);
 #pragma unroll
                         for (int j = 0; j < NSUB; j++)
@@ -523,8 +601,8 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
 #pragma unroll
                 for (int i = 0; i < MSUB; i++) {
                     issue_piece(kb1, st ^ 1, i);
-                    const v8i af = frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
-                    const float sa_i = sSA_w[i * 16];
+                    float sa_i;
+                    const v8i af = next_af(i, sa_i);
 #pragma unroll
                     for (int j = 0; j < NSUB; j++) {
                         const v4f cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -568,6 +646,17 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     }
 
     __builtin_amdgcn_s_waitcnt(0);          // the last step's (redundant) staging loads
+    if constexpr (POW2) {
+        // A scale that is not a positive power of two was applied without its mantissa: the wave's whole
+        // output tile becomes NaN, so the misuse shows instead of giving plausible wrong sums.
+        if (__builtin_amdgcn_ballot_w64(bad_scale != 0) != 0) {
+#pragma unroll
+            for (int i = 0; i < MSUB; i++)
+#pragma unroll
+                for (int j = 0; j < NSUB; j++) acc[i][j] = v4f{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                               __builtin_nanf("")};
+        }
+    }
     // ---------------- epilogue ----------------
     if constexpr (EPI == EPI_QUANT) {
         // The BF16 output, quantized 1x128 along its columns exactly as fg_quantize_act_1x128 would quantize

@@ -48,7 +48,14 @@
  * scale is an exact power of two in [2^-126, 2^127] (what the quantizers write in that mode): the matrix
  * core then applies the scales itself (E8M0 block-scale operands of v_mfma_scale_f32_16x16x128_f8f6f4) and
  * adds 2^(ea+eb) * P_b straight into the FP32 accumulator, which is the same promotion with an exact
- * scale product and no VALU work. Passing FG_SCALE_POW2 with other scales gives unspecified results.
+ * scale product and no VALU work. Passing FG_SCALE_POW2 with a scale that has sign or mantissa bits set
+ * makes the outputs NaN (every output of each 64-column wave tile whose contraction read such a scale;
+ * fg_fp8_gemm_fprop_quant then writes NaN codes 0x7F and NaN scales for those rows). A zero scale reads as
+ * 2^-127 in this mode.
+ *
+ * Size limits of every GEMM (the kernels address operand rows with 32-bit offsets from the tile base):
+ * the contraction length is at most 2^24, and Dgrad's output width (its K) at most 2^25. Larger shapes
+ * return FG_ERR_UNSUPPORTED_SHAPE.
  *
  * Every GEMM picks one of two workgroup tiles per launch (256x192 or 256x256 outputs) from the problem size
  * and the device's compute-unit count; the results are bit-identical either way (every output element

@@ -1,4 +1,6 @@
 """Shared helpers for the GPU parity tests (device placement, comparisons, sampled outputs)."""
+import os
+
 import numpy as np
 import torch
 
@@ -39,6 +41,56 @@ def normwise(y, ref):
     y = np.asarray(y, np.float64).reshape(-1)
     ref = np.asarray(ref, np.float64).reshape(-1)
     return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def elementwise_large(y, ref, frac=0.01):
+    """Elementwise max |y - ref| / |ref| over the entries with |ref| >= frac * max |ref|: the error metric
+    reported beside the normwise gate (entries far below the largest carry no relative precision)."""
+    y = np.asarray(y, np.float64).reshape(-1)
+    ref = np.asarray(ref, np.float64).reshape(-1)
+    big = np.abs(ref) >= frac * max(np.max(np.abs(ref)), 1e-300)
+    if not np.any(big):
+        return 0.0
+    return float(np.max(np.abs(y[big] - ref[big]) / np.abs(ref[big])))
+
+
+# (test id, output, outputs compared, normwise error, elementwise error over large entries), filled by the
+# GEMM parity checks and printed in the session's terminal summary
+GEMM_ERRORS = []
+
+
+def record_gemm_error(what, y, ref):
+    name = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0].split("::")[-1]
+    GEMM_ERRORS.append((name, what, int(np.asarray(ref).size), normwise(y, ref), elementwise_large(y, ref)))
+
+
+def output_tile_points(rows, cols, tile_rows, tile_cols, seed):
+    """One random flat index inside every tile_rows x tile_cols block of a rows x cols output, the ragged
+    edge blocks included: with 64 x 64 blocks every wave's tile of either workgroup shape is sampled, so a
+    tile written to the wrong place or not at all cannot pass unseen."""
+    rng = np.random.default_rng(seed)
+    r0 = np.arange(0, rows, tile_rows, dtype=np.int64)
+    c0 = np.arange(0, cols, tile_cols, dtype=np.int64)
+    R0, C0 = np.meshgrid(r0, c0, indexing="ij")
+    rr = R0 + (rng.random(R0.shape) * np.minimum(tile_rows, rows - R0)).astype(np.int64)
+    cc = C0 + (rng.random(C0.shape) * np.minimum(tile_cols, cols - C0)).astype(np.int64)
+    return (rr * cols + cc).reshape(-1)
+
+
+def stratified_points(rows, cols, n_random, seed):
+    """sample_points plus one point in every 64 x 64 output block."""
+    return np.unique(np.concatenate([sample_points(rows, cols, n_random, seed),
+                                     output_tile_points(rows, cols, 64, 64, seed + 1000)]))
+
+
+def nan_like_out(shape, dtype):
+    """An output buffer filled with NaN, so an element the kernel never writes fails the finiteness check."""
+    return torch.full(shape, float("nan"), dtype=dtype, device=device())
+
+
+def assert_all_written(t, what):
+    bad = int((~torch.isfinite(t)).sum().item())
+    assert bad == 0, f"{what}: {bad} outputs not written (still NaN) or not finite"
 
 
 def bf16_bits_to_f64(b):

@@ -118,6 +118,32 @@ def test_gemm_rejections(L):
     assert L.fg_last_hip_error() == 0
 
 
+def test_gemm_size_limits(L):
+    """Contractions longer than 2^24 and Dgrad outputs wider than 2^25 would overflow the kernels' 32-bit
+    operand offsets: rejected on the host, while the limits themselves pass the shape checks (the calls
+    below that pass them use M == 0 or equivalent empty outputs, so nothing is launched)."""
+    big, bigger = 1 << 24, (1 << 24) + 128
+    f = L.fg_fp8_gemm_fprop
+    assert f(A16, A16, A16, A16, 128, 128, bigger, A16, 0, 0, None) == SHAPE
+    assert L.fg_fp8_gemm_fprop_quant(A16, A16, A16, A16, 128, 128, bigger, A16, A16, 0, 0, None) == SHAPE
+    d = L.fg_fp8_gemm_dgrad
+    assert d(A16, A16, A16, A16, 128, bigger, 128, A16, 0, 0, None) == SHAPE          # contraction N
+    assert d(A16, A16, A16, A16, 128, 128, (1 << 25) + 128, A16, 0, 0, None) == SHAPE  # output width K
+    w = L.fg_fp8_gemm_wgrad
+    assert w(A16, A16, A16, A16, bigger, 128, 128, A16, 0, 0, None) == SHAPE          # tokens
+    g = L.fg_fp8_grouped_gemm
+    assert g(A16, A16, A16, A16, A16B, 2, 128, 128, bigger, A16, 0, 0, None) == SHAPE
+    gd = L.fg_fp8_grouped_gemm_dgrad
+    assert gd(A16, A16, A16, A16, A16B, 2, 128, bigger, 128, A16, 0, 0, None) == SHAPE
+    assert gd(A16, A16, A16, A16, A16B, 2, 128, 128, (1 << 25) + 128, A16, 0, 0, None) == SHAPE
+    gw = L.fg_fp8_grouped_gemm_wgrad
+    assert gw(A16, A16, A16, A16, A16B, 2, bigger, 128, 128, A16, 0, 0, None) == SHAPE
+    # at the limits the shape checks pass; with an empty output nothing is launched
+    assert f(None, None, None, None, 0, 128, big, None, 0, 0, None) == OK
+    assert w(None, None, None, None, big, 0, 128, None, 0, 0, None) == OK
+    assert L.fg_last_hip_error() == 0
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(fg.Fp8fgError):

@@ -3,8 +3,10 @@
 Gate: normwise max relative error against the oracle's per-128 FP32-promoted result, <= 1e-3 for FP32
 outputs and <= 1e-2 for BF16 outputs (oracle rounded to BF16 too). The matrix core's summation inside
 a 128-element block is hardware-defined, so results are not bit-identical; small shapes are compared in
-full, the full-size workloads on sampled outputs (corners, last row/column, random points) computed one
-by one by the oracle, in the same launch configuration the benchmark times.
+full, the full-size workloads on sampled outputs computed one by one by the oracle, in the same launch
+configuration the benchmark times: corners, the last row and column, random points, and one point in
+every 64 x 64 output block (so every wave's tile of either workgroup shape is sampled). Every output
+buffer starts filled with NaN and must come back entirely finite, so an element no kernel writes fails.
 """
 import numpy as np
 import pytest
@@ -13,8 +15,8 @@ import torch
 import fp8_fine_grained_amax_amd as fg
 import oracle
 from fp8_fine_grained_amax_amd import workloads as wl
-from tests.gpu_util import (TOL_BF16, TOL_F32, bf16_bits_to_f64, bits, device, normwise, np_u8, sample_points,
-                            to_dev)
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_all_written, bf16_bits_to_f64, bits, device, nan_like_out,
+                            normwise, np_u8, record_gemm_error, sample_points, stratified_points, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +29,14 @@ def _out_np(y, bf16):
 
 def _cmp(y_gpu, prom, bf16, tol_scale=1.0):
     if bf16:
-        err = normwise(bf16_bits_to_f64(np.asarray(y_gpu).reshape(-1)), bf16_bits_to_f64(np.asarray(prom).reshape(-1)))
+        a, b = bf16_bits_to_f64(np.asarray(y_gpu).reshape(-1)), bf16_bits_to_f64(np.asarray(prom).reshape(-1))
+        err = normwise(a, b)
+        record_gemm_error("bf16", a, b)
         assert err <= TOL_BF16 * tol_scale, err
     else:
-        err = normwise(np.asarray(y_gpu).reshape(-1), np.asarray(prom).reshape(-1))
+        a, b = np.asarray(y_gpu).reshape(-1), np.asarray(prom).reshape(-1)
+        err = normwise(a, b)
+        record_gemm_error("f32", a, b)
         assert err <= TOL_F32 * tol_scale, err
     return err
 
@@ -61,8 +67,10 @@ def _rand_act(rng, rows, cols, std=1.0):
 def _fprop_case(x, w, bf16, pow2=False, pts=None):
     xq, sx = fg.fg_quantize_act_1x128(to_dev(x), pow2=pow2)
     wq, sw = fg.fg_quantize_w_128x128(to_dev(w), pow2=pow2)
-    y = fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.bfloat16 if bf16 else torch.float32, pow2=pow2)
+    y = nan_like_out((x.shape[0], w.shape[0]), torch.bfloat16 if bf16 else torch.float32)
+    fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, y=y, pow2=pow2)
     torch.cuda.synchronize()
+    assert_all_written(y, "fprop")
     xq_n, sx_n, wq_n, sw_n = np_u8(xq), sx.cpu().numpy(), np_u8(wq), sw.cpu().numpy()
     # the codes the GEMM consumed are the oracle's codes (checked bit-exact in the quantizer tests);
     # re-derive them here from the oracle so the GEMM check does not trust the GPU quantizer
@@ -137,7 +145,7 @@ def test_fprop_dsv3_full_size_sampled(dsv3, pow2):
     x, w, _ = dsv3
     M, K = x.shape
     N = w.shape[0]
-    pts = sample_points(M, N, 3000, seed=11)
+    pts = stratified_points(M, N, 3000, seed=11)
     err, y, exact = _fprop_case(x, w, bf16=True, pow2=pow2, pts=pts)
     assert normwise(bf16_bits_to_f64(y), exact) <= TOL_BF16
 
@@ -158,8 +166,10 @@ def test_fprop_deterministic(dsv3):
 def _dgrad_case(dy, w, bf16, pts=None, pow2=False):
     dyq, sdy = fg.fg_quantize_act_1x128(to_dev(dy), pow2=pow2)
     wq, sw = fg.fg_quantize_w_128x128(to_dev(w), pow2=pow2)
-    dx = fg.fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, out_dtype=torch.bfloat16 if bf16 else torch.float32, pow2=pow2)
+    dx = nan_like_out((dy.shape[0], w.shape[1]), torch.bfloat16 if bf16 else torch.float32)
+    fg.fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, dx=dx, pow2=pow2)
     torch.cuda.synchronize()
+    assert_all_written(dx, "dgrad")
     dyq_o, sdy_o = oracle.quantize_act_1x128(bits(dy), 0, pow2)
     wq_o, sw_o = oracle.quantize_w_128x128(bits(w), pow2)
     assert np.array_equal(np_u8(dyq), dyq_o) and np.array_equal(np_u8(wq), wq_o)
@@ -184,7 +194,7 @@ def test_dgrad_dsv3_full_size_sampled(dsv3, pow2):
     x, w, dy = dsv3
     M, N = dy.shape
     K = w.shape[1]
-    pts = sample_points(M, K, 2000, seed=12)
+    pts = stratified_points(M, K, 2000, seed=12)
     err, y, exact = _dgrad_case(dy, w, bf16=False, pts=pts, pow2=pow2)
     assert normwise(y, exact) <= TOL_F32
 
@@ -201,8 +211,10 @@ def _wgrad_case(dy, x, pts=None, init=None, pow2=False):
         dw = to_dev(torch.from_numpy(init))
         dw = fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw, accumulate=True, pow2=pow2)
     else:
-        dw = fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, pow2=pow2)
+        dw = nan_like_out((N, K), torch.float32)
+        fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw, pow2=pow2)
     torch.cuda.synchronize()
+    assert_all_written(dw, "wgrad")
     dytq_o, sdyt_o = oracle.quantize_act_1x128(bits(dy), 1, pow2)
     xtq_o, sxt_o = oracle.quantize_act_1x128(bits(x), 1, pow2)
     assert np.array_equal(np_u8(dytq), dytq_o) and np.array_equal(np_u8(xtq), xtq_o)
@@ -236,7 +248,7 @@ def test_wgrad_accumulate(pow2, tile):
 def test_wgrad_dsv3_full_size_sampled(dsv3, pow2):
     x, w, dy = dsv3
     N, K = dy.shape[1], x.shape[1]
-    pts = sample_points(N, K, 2000, seed=13)
+    pts = stratified_points(N, K, 2000, seed=13)
     err, y, exact = _wgrad_case(dy, x, pts=pts, pow2=pow2)
     assert normwise(y, exact) <= TOL_F32
 
@@ -254,13 +266,17 @@ def _grouped_case(x, w, offsets, bf16=True, pts=None, pow2=False):
     for g in range(G):
         fg.fg_quantize_w_128x128(wd[g], q=wq[g], scales=sw[g], pow2=pow2)
     off = torch.from_numpy(np.asarray(offsets, np.int32)).to(device())
-    y = fg.fg_fp8_grouped_gemm(xq, sx, wq, sw, off, out_dtype=torch.bfloat16 if bf16 else torch.float32, pow2=pow2)
+    y = nan_like_out((x.shape[0], N), torch.bfloat16 if bf16 else torch.float32)
+    fg.fg_fp8_grouped_gemm(xq, sx, wq, sw, off, y=y, pow2=pow2)
     torch.cuda.synchronize()
+    assert_all_written(y, "grouped")
     xq_o, sx_o = oracle.quantize_act_1x128(bits(x), 0, pow2)
     assert np.array_equal(np_u8(xq), xq_o)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_o.view(np.uint32)), "activation scales"
     wo = [oracle.quantize_w_128x128(bits(w[g]), pow2) for g in range(G)]
     wq_o, sw_o = np.stack([a for a, _ in wo]), np.stack([b for _, b in wo])
     assert np.array_equal(np_u8(wq), wq_o)
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_o.view(np.uint32)), "weight scales"
     prom, exact = oracle.gemm_grouped(xq_o, sx_o, wq_o, sw_o, offsets, out_bf16=bf16, pts=pts)
     yo = _out_np(y, bf16).reshape(-1)
     yo = yo if pts is None else yo[pts]
@@ -280,22 +296,25 @@ def test_grouped_small_with_empty_groups(bf16, pow2, tile):
     _grouped_case(x, w, offsets, bf16, pow2=pow2)
 
 
-def test_grouped_moe_share_full_size_sampled():
+def test_grouped_moe_share_full_size_sampled(moe_share):
     device()
-    d = wl.moe_inputs()
+    d = moe_share
     T = int(d["offsets"][-1])
     assert T == wl.MOE_TOKENS * wl.MOE_TOPK
-    pts = sample_points(T, wl.MOE_INTER, 2000, seed=14)
+    pts = stratified_points(T, wl.MOE_INTER, 2000, seed=14)
     err, y, exact = _grouped_case(d["x"], d["w_up"], d["offsets"], bf16=True, pts=pts)
     assert normwise(bf16_bits_to_f64(y), exact) <= TOL_BF16
 
 
-def test_grouped_moe_down_projection_sampled():
+def test_grouped_moe_down_projection_full_size_sampled(moe_share):
+    """The down-projection at all 65536 routed rows: H [65536, 2048] . W_down[e]^T -> [65536, 7168]."""
     device()
-    d = wl.moe_inputs(rows_scale=0.25)
+    d = moe_share
     T = int(d["offsets"][-1])
-    pts = sample_points(T, wl.MOE_HIDDEN, 2000, seed=15)
-    _grouped_case(d["h"], d["w_down"], d["offsets"], bf16=True, pts=pts)
+    assert T == wl.MOE_TOKENS * wl.MOE_TOPK
+    pts = stratified_points(T, wl.MOE_HIDDEN, 2000, seed=15)
+    err, y, exact = _grouped_case(d["h"], d["w_down"], d["offsets"], bf16=True, pts=pts)
+    assert normwise(bf16_bits_to_f64(y), exact) <= TOL_BF16
 
 
 # ------------------------------------------------------------------------------------------------
@@ -312,9 +331,10 @@ def _grouped_dgrad_case(dy, w, offsets, bf16=False, pts_per_group=None, pow2=Fal
     for g in range(G):
         fg.fg_quantize_w_128x128(wd[g], q=wq[g], scales=sw[g], pow2=pow2)
     off = torch.from_numpy(np.asarray(offsets, np.int32)).to(device())
-    dx = fg.fg_fp8_grouped_gemm_dgrad(dyq, sdy, wq, sw, off, out_dtype=torch.bfloat16 if bf16 else torch.float32,
-                                      pow2=pow2)
+    dx = nan_like_out((dy.shape[0], K), torch.bfloat16 if bf16 else torch.float32)
+    fg.fg_fp8_grouped_gemm_dgrad(dyq, sdy, wq, sw, off, dx=dx, pow2=pow2)
     torch.cuda.synchronize()
+    assert_all_written(dx, "grouped dgrad")
     dyq_o, sdy_o = oracle.quantize_act_1x128(bits(dy), 0, pow2)
     assert np.array_equal(np_u8(dyq), dyq_o)
     out = _out_np(dx, bf16)
@@ -324,7 +344,7 @@ def _grouped_dgrad_case(dy, w, offsets, bf16=False, pts_per_group=None, pow2=Fal
         if r1 == r0:
             continue
         wq_o, sw_o = oracle.quantize_w_128x128(bits(w[g]), pow2)
-        pts = None if pts_per_group is None else sample_points(r1 - r0, K, pts_per_group, seed=31 + g)
+        pts = None if pts_per_group is None else stratified_points(r1 - r0, K, pts_per_group, seed=31 + g)
         prom, _ = oracle.gemm_dgrad(dyq_o[r0:r1], np.ascontiguousarray(sdy_o[:, r0:r1]), wq_o, sw_o, out_bf16=bf16,
                                     pts=pts)
         yo = out[r0:r1].reshape(-1)
@@ -364,8 +384,10 @@ def _grouped_wgrad_case(dy, x, offsets, init=None, pts_per_group=None, pow2=Fals
         dw = fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, off, dw=to_dev(torch.from_numpy(init)), accumulate=True,
                                           pow2=pow2)
     else:
-        dw = fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, off, pow2=pow2)
+        dw = nan_like_out((G, N, K), torch.float32)
+        fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, off, dw=dw, pow2=pow2)
     torch.cuda.synchronize()
+    assert_all_written(dw, "grouped wgrad")
     dytq_o, sdyt_o = oracle.quantize_act_1x128(bits(dy), 1, pow2)
     xtq_o, sxt_o = oracle.quantize_act_1x128(bits(x), 1, pow2)
     assert np.array_equal(np_u8(dytq), dytq_o) and np.array_equal(np_u8(xtq), xtq_o)
@@ -373,7 +395,7 @@ def _grouped_wgrad_case(dy, x, offsets, init=None, pts_per_group=None, pow2=Fals
     errs = []
     for g in range(G):
         t0, t1 = int(offsets[g]), int(offsets[g + 1])
-        pts = None if pts_per_group is None else sample_points(N, K, pts_per_group, seed=41 + g)
+        pts = None if pts_per_group is None else stratified_points(N, K, pts_per_group, seed=41 + g)
         init_g = None if init is None else (init[g].reshape(-1) if pts is None else init[g].reshape(-1)[pts])
         prom, _ = oracle.gemm_wgrad(np.ascontiguousarray(dytq_o[:, t0:t1]), np.ascontiguousarray(sdyt_o[t0 // 128: t1 // 128]),
                                     np.ascontiguousarray(xtq_o[:, t0:t1]), np.ascontiguousarray(sxt_o[t0 // 128: t1 // 128]),
@@ -454,6 +476,63 @@ def test_grouped_offsets_clamped_on_device():
     torch.cuda.synchronize()
     for name, a, b in (("fprop", y_good, y_bad), ("dgrad", dx_good, dx_bad), ("wgrad", dw_good, dw_bad)):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+
+
+# ------------------------------------------------------------------------------------------------
+# Power-of-2 mode handed scales that are not powers of two: NaN outputs, not silently wrong sums
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tile", TILES, indirect=True)
+def test_pow2_mode_poisons_tiles_with_other_scales(tile):
+    """Power-of-2 codes and scales, with one activation row's scale given mantissa bits: every output of
+    the wave tiles that read that scale is NaN, every other output equals the clean run bit for bit."""
+    device()
+    rng = np.random.default_rng(91)
+    M, N, K = 300, 520, 384
+    xq, sx = fg.fg_quantize_act_1x128(to_dev(_rand_act(rng, M, K)), pow2=True)
+    wq, sw = fg.fg_quantize_w_128x128(to_dev(wl.normal_bf16(rng, (N, K), 0.02)), pow2=True)
+    clean = fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.float32, pow2=True)
+    bad_sx = sx.clone()
+    bad_sx[1, 5] *= 1.5                                  # row 5, second 128-block: not a power of two
+    y = fg.fg_fp8_gemm_fprop(xq, bad_sx, wq, sw, out_dtype=torch.float32, pow2=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(y[5]).all(), "the row whose scale has mantissa bits must be NaN"
+    assert torch.isfinite(y[128:]).all() and torch.equal(y[128:].view(torch.int32), clean[128:].view(torch.int32))
+    finite_rows = torch.isfinite(y).all(dim=1)
+    assert torch.equal(y[finite_rows].view(torch.int32), clean[finite_rows].view(torch.int32))
+
+
+def test_pow2_mode_with_fp32_scales_is_nan_everywhere():
+    """FP32-mode scales (almost none a power of two) declared as power-of-2 scales: every GEMM entry point
+    returns NaN outputs (and NaN codes and scales from the quantizing Fprop)."""
+    device()
+    rng = np.random.default_rng(92)
+    M, N, K = 256, 384, 512
+    x, w = to_dev(_rand_act(rng, M, K)), to_dev(wl.normal_bf16(rng, (N, K), 0.02))
+    dy = to_dev(_rand_act(rng, M, N, 1e-3))
+    xq, sx = fg.fg_quantize_act_1x128(x)
+    wq, sw = fg.fg_quantize_w_128x128(w)
+    dyq, sdy = fg.fg_quantize_act_1x128(dy)
+    dytq, sdyt = fg.fg_quantize_act_1x128(dy, axis=fg.FG_ALONG_ROWS)
+    xtq, sxt = fg.fg_quantize_act_1x128(x, axis=fg.FG_ALONG_ROWS)
+    off = torch.tensor([0, 100, M], dtype=torch.int32, device=device())
+    offw = torch.tensor([0, 128, M], dtype=torch.int32, device=device())
+    outs = {
+        "fprop": fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, out_dtype=torch.float32, pow2=True),
+        "fprop_bf16": fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, pow2=True),
+        "dgrad": fg.fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, pow2=True),
+        "wgrad": fg.fg_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, pow2=True),
+        "grouped": fg.fg_fp8_grouped_gemm(xq, sx, torch.stack([wq, wq]), torch.stack([sw, sw]), off, pow2=True),
+        "grouped_dgrad": fg.fg_fp8_grouped_gemm_dgrad(dyq, sdy, torch.stack([wq, wq]), torch.stack([sw, sw]), off,
+                                                      pow2=True),
+        "grouped_wgrad": fg.fg_fp8_grouped_gemm_wgrad(dytq, sdyt, xtq, sxt, offw, pow2=True),
+    }
+    yq, sy = fg.fg_fp8_gemm_fprop_quant(xq, sx, wq, sw, pow2=True)
+    torch.cuda.synchronize()
+    for name, t in outs.items():
+        assert torch.isnan(t.float()).all(), name
+    assert torch.isnan(sy).all()
+    assert bool(((yq & 0x7F) == 0x7F).all()), "quantizing Fprop: NaN codes"
 
 
 @pytest.mark.parametrize("pow2", [False, True])

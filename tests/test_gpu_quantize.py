@@ -78,13 +78,19 @@ def test_dsv3_backward_token_dim(dsv3):
     _check_act(dsv3[0], fg.FG_ALONG_ROWS, False)      # X^T for Wgrad
 
 
-def test_moe_share_inputs():
+@pytest.mark.parametrize("pow2", [False, True])
+def test_moe_share_inputs_full_size(moe_share, pow2):
+    """One GPU's MoE share at its stated size: X [65536, 7168] and H [65536, 2048] (the up- and
+    down-projection inputs), codes and scales bit-exact, and every expert's W_up and W_down blocks."""
     device()
-    d = wl.moe_inputs(rows_scale=0.125)
-    _check_act(d["x"], fg.FG_ALONG_COLS, False)
-    _check_act(d["h"], fg.FG_ALONG_COLS, True)
-    _check_w(d["w_up"][0], False)
-    _check_w(d["w_down"][3], False)
+    d = moe_share
+    assert d["x"].shape == (wl.MOE_TOKENS * wl.MOE_TOPK, wl.MOE_HIDDEN)
+    assert d["h"].shape == (wl.MOE_TOKENS * wl.MOE_TOPK, wl.MOE_INTER)
+    _check_act(d["x"], fg.FG_ALONG_COLS, pow2)
+    _check_act(d["h"], fg.FG_ALONG_COLS, pow2)
+    for e in range(wl.MOE_EXPERTS):
+        _check_w(d["w_up"][e], pow2)
+        _check_w(d["w_down"][e], pow2)
 
 
 @pytest.mark.parametrize("rows,cols,ld_pad", [(1, 128, 0), (37, 384, 8), (65, 1024, 0), (1000, 256, 24)])
@@ -165,6 +171,59 @@ def test_every_finite_bf16_value(pow2):
     xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
     _check_act(xt, fg.FG_ALONG_COLS, pow2)
     _check_act(xt[:, :128].contiguous()[: (x.shape[0] // 128) * 128], fg.FG_ALONG_ROWS, pow2)
+
+
+def _amax_mantissa_rows(exponents=(0x20, 0x3F, 0x7F, 0x85, 0xC0)):
+    """bf16 rows of 128 whose max-abs runs over all 128 bf16 mantissas at several exponents, with both
+    signs and the max at a varying position; every other entry is smaller in magnitude, of random sign.
+    In fp32-scale mode the quotient max / RN(max / 448) comes out as 448 * (1 + 2^-23) in fp32 for some of
+    these mantissas, and the encoder must still give the code of 448."""
+    rng = np.random.default_rng(77)
+    rows = []
+    for e in exponents:
+        for m in range(128):
+            for sign in (0, 1):
+                top = (e << 7) | m
+                rest = rng.integers(0, top, 127).astype(np.uint16) | (rng.integers(0, 2, 127).astype(np.uint16) << 15)
+                pos = int(rng.integers(0, 128))
+                rows.append(np.insert(rest, pos, np.uint16((sign << 15) | top)))
+    return np.stack(rows).astype(np.uint16)
+
+
+def _assert_max_code_448(q_tiles):
+    """Every tile (last axis) holds a code of magnitude 448 (0x7E or 0xFE)."""
+    mags = np.asarray(q_tiles) & 0x7F
+    assert np.all(mags.max(axis=-1) == 0x7E), "a tile whose max-abs should encode to 448 does not"
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quotient_at_448_every_mantissa(pow2):
+    """Deterministic cover of the quotient edge above 448: 1x128 tiles along the columns and along the
+    rows, both tilings from one read, and 128x128 weight blocks, each with its max-abs on every bf16
+    mantissa (five exponents, both signs); bit-exact against the oracle, and in fp32-scale mode every
+    tile's largest code is 448."""
+    device()
+    t = _amax_mantissa_rows()                                     # [1280, 128]
+    x = torch.from_numpy(t.view(np.int16)).view(torch.bfloat16)
+    _check_act(x, fg.FG_ALONG_COLS, pow2)
+    xt = torch.from_numpy(np.ascontiguousarray(t.T).view(np.int16)).view(torch.bfloat16)   # [128, 1280]
+    _check_act(xt, fg.FG_ALONG_ROWS, pow2)
+    _check_both(x, pow2)
+    # weight blocks: block b is 128 rows of smaller entries plus the tile's max-abs entry in its first row
+    rng = np.random.default_rng(78)
+    nb = t.shape[0] // 8                                          # 160 blocks, every 8th row's max-abs
+    wb = np.empty((nb * 128, 128), np.uint16)
+    for b in range(nb):
+        top = int(np.max(t[8 * b] & 0x7FFF))
+        blk = rng.integers(0, top, (128, 128)).astype(np.uint16) | (rng.integers(0, 2, (128, 128)).astype(np.uint16) << 15)
+        blk[0] = t[8 * b]
+        wb[b * 128:(b + 1) * 128] = blk
+    _check_w(torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16), pow2)
+    if not pow2:
+        q, _ = fg.fg_quantize_act_1x128(to_dev(x))
+        _assert_max_code_448(np_u8(q))
+        qw, _ = fg.fg_quantize_w_128x128(to_dev(torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16)))
+        _assert_max_code_448(np_u8(qw).reshape(nb, 128 * 128))
 
 
 def test_deterministic_repeat(dsv3):
