@@ -132,9 +132,6 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
     return x * base + (x < extra ? x : extra) + local;
 }
 
-#ifndef FG_BUFFER_LOADS
-#define FG_BUFFER_LOADS 1
-#endif
 // Raw buffer descriptor over [base, base + 2^32 - 1): stride 0, no swizzle; the range check never
 // triggers for the 32-bit offsets the kernels use (the host bounds the sizes so they stay below 2^32).
 // The base is wave-uniform by construction; taking it through readfirstlane states so, and the descriptor
@@ -155,6 +152,11 @@ __device__ __forceinline__ void fg_buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FG_LDS(lds), 16, voffset, 0, 0, 0);
 #endif
 }
+
+template <bool B>
+struct fg_bool {
+    static constexpr bool value = B;
+};
 
 // A device-resident group offset clamped into [lo, hi].
 __device__ __forceinline__ int64_t fg_clamp_offset(int32_t v, int64_t lo, int64_t hi) {
@@ -349,7 +351,6 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
 
     // Load q of the wave's LOADS_PER_WAVE for K step kb into stage st: A instructions, then B, then the
     // scale slice. `issue_piece(kb, st, i)` issues the i-th of MSUB near-equal pieces of that sequence.
-#if FG_BUFFER_LOADS
     // Buffer-descriptor form of the direct-to-LDS loads: a wave-uniform base (rebuilt per K step in SGPRs)
     // plus the lane's 32-bit offset. Unlike the global form, which the compiler must treat as a pending
     // LDS access of unknown order, it leaves the LDS fragment reads countable one by one, so a wait for
@@ -369,27 +370,13 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                                                      0, 0, 0);
         }
     };
-#else
-    auto issue_load = [&](int kb, int st, int q) {
-        if (q < C::UA) {
-            const uint8_t* a_k = a_tile + (int64_t)kb * BK;
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(a_k + a_off[q]), FG_LDS(stA(st) + a_t[q] * 1024), 16, 0, 0);
-        } else if (q < C::UA + C::UB) {
-            const int u = q - C::UA;
-            const uint8_t* b_k = B_TRANS ? b_tile + (int64_t)kb * BK * N : b_tile + (int64_t)kb * BK;
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(b_k + b_off[u]), FG_LDS(stB(st) + b_t[u] * 1024), 16, 0, 0);
-        } else {
-            const float* src = sc_is_b ? SBp + (int64_t)kb * N + sc_row : SAp + (int64_t)kb * p.sa_ld + sc_row;
-            __builtin_amdgcn_global_load_lds(FG_GLOBAL(src), FG_LDS(reinterpret_cast<uint8_t*>(stSA(st)) + sc_dst), 4,
-                                             0, 0);
-        }
-    };
-#endif
+
     // Pieces go out ahead of the first F MFMA rows of the step (loads issued early have longer to land;
     // loads spread out disturb the MFMA stream less). Measured per shape on the dense-MLP GEMMs:
     // 256x192: F = 2; 256x256 with 128x128 weight blocks (Fprop, Dgrad): F = 3; per-row B scales (Wgrad):
-    // spread over all rows.
-    constexpr int F = C::NW == 12 ? 2 : (SBK == SB_ROW ? MSUB : 3);
+    // spread over every row but the last (the loads must be out before the step's hand-over barrier).
+    constexpr int F = C::NW == 12 ? 2 : (SBK == SB_ROW ? MSUB - 1 : 3);
+    static_assert(F <= MSUB - 1, "the next stage's loads are all issued before the last row's hand-over barrier");
     // Dgrad (transposed B: its fragment reads are the slowest LDS traffic) raises the wave's priority while
     // it issues a row of MFMAs, so the SIMD keeps the matrix core fed ahead of other waves' loads and LDS
     // reads: measured 3-5% faster there, and slower for the other GEMMs, which keep the default.
@@ -460,55 +447,64 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     }
 
     // ---------------- main loop ----------------
-    // The 128x128 block scale of step kb+1 is fetched with that step's tile loads, so the wait at the top
-    // of each step covers it and no step waits on a scale load of its own.
+    // Step kb computes from stage kb & 1 while the loads of step kb+1 fill the other stage. The barrier that
+    // hands the next stage over sits just before each step's last row of MFMAs: every read of the current
+    // stage is done by then (the last row's A fragment is already in registers), and the next step's B
+    // fragments and first A fragment are read while that last row issues, so no step starts with every
+    // wave of the SIMD waiting on LDS. The 128x128 block scale of step kb+1 is fetched one step ahead.
     float sb_next = 1.0f;
     uint32_t bad_scale = 0;                 // power-of-2 mode: sign or mantissa bits seen in any scale
+    // Two A register sets fit wherever the promotion leaves 8 registers free; the FP32-scale Wgrad
+    // (per-row B scales) and the 256x256 FP32-scale Fprop read each row's fragment just before it.
+    constexpr bool AF_AHEAD = POW2 || SBK == SB_BLOCK_T || (C::NW == 12 && SBK == SB_BLOCK);
+    v8i bf[NSUB];                           // B-role fragments of the wave's NSUB N tiles, one K step
+    float4 sbr[NSUB];                       // per-row B scales (FP32 mode) of the lane's 4 output columns
+    int ebr[NSUB];                          // per-row B scales (power-of-2 mode) as E8M0, column lrow
+    v8i af_next;                            // the next row's A fragment and A-row scale
+    float sa_next = 0.f;
+    auto read_b = [&](int st, int j) {
+        const uint8_t* sBs = stB(st);
+        if constexpr (!B_TRANS) {
+            bf[j] = frag_at(sBs + (wn * WAVE_N + j * 16) * BK, frag_lo, frag_hi);
+        } else {
+            const int chunk = wn * (WAVE_N / 16) + j;
+            v2i part[4];
+#pragma unroll
+            for (int h = 0; h < 4; h++)
+                part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(sBs + tr_off[h] + ((chunk ^ tr_z[h]) << 4)));
+            bf[j] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+        }
+        if constexpr (SBK == SB_ROW) {
+            if constexpr (POW2) ebr[j] = e8m0_of(stSB(st)[wn * WAVE_N + j * 16 + lrow], bad_scale);
+            else sbr[j] = *reinterpret_cast<const float4*>(stSB(st) + wn * WAVE_N + j * 16 + lcol4);
+        }
+    };
+    auto read_a0 = [&](int st) {
+        af_next = frag_at(stA(st) + wm * WAVE_M * BK, frag_lo, frag_hi);
+        sa_next = stSA(st)[wm * WAVE_M + lrow];
+    };
     if (nkb > 0) {
 #pragma unroll
         for (int q = 0; q < C::LOADS_PER_WAVE; q++) issue_load(0, 0, q);
         sb_next = block_scale(0);
-    }
-    for (int kb = 0; kb < nkb; kb++) {
-        const int st = kb & 1;
-        const float sb_blk = sb_next;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        // next step's stage (on the last step: a harmless reload of this step's data into the idle buffer,
-        // which keeps the step body branch-free)
-        const int kb1 = kb + 1 < nkb ? kb + 1 : kb;
-        sb_next = block_scale(kb1);
-        const uint8_t* sAs = stA(st);
-        const uint8_t* sBs = stB(st);
-        const float* sSA = stSA(st);
-        const uint8_t* sA_w = sAs + wm * WAVE_M * BK;
-        const float* sSA_w = sSA + wm * WAVE_M + lrow;
-        // A-role fragments are read one row of tiles ahead (two register sets): the first row's is read
-        // before the B fragments, so the step's first MFMA waits only for the reads it needs, and every
-        // later row's read has the previous row's MFMAs to land behind.
-        v8i af_next = frag_at(sA_w, frag_lo, frag_hi);
-        float sa_next = sSA_w[0];
-        // B-role fragments for the wave's NSUB N tiles, held for the whole K step
-        v8i bf[NSUB];
+        read_a0(0);
 #pragma unroll
-        for (int j = 0; j < NSUB; j++) {
-            if constexpr (!B_TRANS) {
-                bf[j] = frag_at(sBs + (wn * WAVE_N + j * 16) * BK, frag_lo, frag_hi);
-            } else {
-                const int chunk = wn * (WAVE_N / 16) + j;
-                v2i part[4];
-#pragma unroll
-                for (int h = 0; h < 4; h++)
-                    part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) v2i*)(sBs + tr_off[h] + ((chunk ^ tr_z[h]) << 4)));
-                bf[j] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
-            }
-        }
-        // Two A register sets fit wherever the promotion leaves 8 registers free; the FP32-scale Wgrad
-        // (per-row B scales) and the 256x256 FP32-scale Fprop read each row's fragment just before it.
-        constexpr bool AF_AHEAD = POW2 || SBK == SB_BLOCK_T || (C::NW == 12 && SBK == SB_BLOCK);
-        // Row i's A fragment and A-row scale (the scale is read with the fragment, so waiting for one
-        // never waits for reads issued after it).
+        for (int j = 0; j < NSUB; j++) read_b(0, j);
+    }
+    // One K step; MORE: a next step exists (every step but the last), a compile-time flag so that no
+    // register set is kept alive across the loop's back edge for a path that leaves the loop.
+    auto step = [&](int kb, auto more_tag) {
+        constexpr bool more = decltype(more_tag)::value;
+        const int st = kb & 1;
+        const float sb_blk = sb_next;
+        if (more) sb_next = block_scale(kb + 1);
+        const uint8_t* sA_w = stA(st) + wm * WAVE_M * BK;
+        const float* sSA_w = stSA(st) + wm * WAVE_M + lrow;
+        // Row i's A fragment and A-row scale (the scale is read with the fragment, so waiting for one never
+        // waits for reads issued after it). The last row's is in registers before the hand-over barrier.
         auto next_af = [&](int i, float& sa) -> v8i {
             if constexpr (AF_AHEAD) {
                 const v8i af = af_next;
@@ -523,28 +519,50 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                 return i == 0 ? af_next : frag_at(sA_w + i * 16 * BK, frag_lo, frag_hi);
             }
         };
+        // Before the last row: wait for this wave's loads of the next stage, then for every wave's.
+        // The scheduling fences keep the compiler from moving MFMAs of the earlier rows past the barrier
+        // (which would shorten the time the next stage's loads have to land).
+        auto hand_over = [&](int i) {
+            if (more && i == MSUB - 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (AF_AHEAD) read_a0(st ^ 1);
+            }
+        };
+        // After the last row's MFMA j has issued, its B fragment register takes the next step's.
+        auto after_mfma = [&](int i, int j) {
+            if (more && i == MSUB - 1) {
+                read_b(st ^ 1, j);
+                if constexpr (!AF_AHEAD)
+                    if (j == NSUB - 1) read_a0(st ^ 1);
+            }
+        };
+        auto load_piece = [&](int i) {
+            if (more) issue_piece(kb + 1, st ^ 1, i);
+        };
         if constexpr (POW2) {
             // Power-of-two scales: the matrix core applies them itself. Per lane l the E8M0 scale operand
             // of a 16x128 fragment scales row l%16 (all four 32-element K sub-blocks of the lane carry the
             // same scale), so the A-role operand takes the row scale of output row m and the B-role
             // operand the block scale (or, with per-row B scales, the scale of output column n); the MFMA
             // adds 2^(ea+eb) * P_b straight into the FP32 accumulator, with no VALU promotion.
-            int eb[NSUB];
-#pragma unroll
-            for (int j = 0; j < NSUB; j++)
-                eb[j] = SBK == SB_ROW ? e8m0_of(stSB(st)[wn * WAVE_N + j * 16 + lrow], bad_scale)
-                                      : e8m0_of(sb_blk, bad_scale);
+            const int eb_blk = SBK == SB_ROW ? 0 : e8m0_of(sb_blk, bad_scale);
 #pragma unroll
             for (int i = 0; i < MSUB; i++) {
-                issue_piece(kb1, st ^ 1, i);
+                load_piece(i);
                 float sa_i;
                 const v8i af = next_af(i, sa_i);
                 const int ea = e8m0_of(sa_i, bad_scale);
+                hand_over(i);
                 if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(MFMA_PRIO);
 #pragma unroll
-                for (int j = 0; j < NSUB; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, eb[j], 0,
-                                                                                ea);
+                for (int j = 0; j < NSUB; j++) {
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf[j], af, acc[i][j], 0, 0, 0, SBK == SB_ROW ? ebr[j] : eb_blk, 0, ea);
+                    after_mfma(i, j);
+                }
                 if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
             }
         } else {
@@ -553,13 +571,6 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
             // (8-wave shape, one scale per lane) the FMAs that fold row i-1 into the FP32 accumulators
             // follow the MFMAs of row i; otherwise the FMAs of each tile follow the next tile's MFMA.
             constexpr bool ROW_PIPE = C::NW == 8 && SBK != SB_ROW;
-            float4 sbr[NSUB];
-            if constexpr (SBK == SB_ROW) {
-                const float* sSB = stSB(st);
-#pragma unroll
-                for (int j = 0; j < NSUB; j++)
-                    sbr[j] = *reinterpret_cast<const float4*>(sSB + wn * WAVE_N + j * 16 + lcol4);
-            }
             if constexpr (ROW_PIPE) {
                 v4f prev[NSUB], cur[NSUB];
                 float sa_prev = 0.f;
@@ -567,13 +578,16 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                 for (int i = 0; i <= MSUB; i++) {
                     float sa_i = 0.f;
                     if (i < MSUB) {
-                        issue_piece(kb1, st ^ 1, i);
+                        load_piece(i);
                         const v8i af = next_af(i, sa_i);
+                        hand_over(i);
                         if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(MFMA_PRIO);
 #pragma unroll
-                        for (int j = 0; j < NSUB; j++)
+                        for (int j = 0; j < NSUB; j++) {
                             cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, v4f{0.f, 0.f, 0.f, 0.f},
                                                                                      0, 0, 0, 127, 0, 127);
+                            after_mfma(i, j);
+                        }
                         if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
                     }
                     if (i > 0) {
@@ -600,9 +614,10 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                 for (int l = 0; l < LAG; l++) pend_i[l] = -1;
 #pragma unroll
                 for (int i = 0; i < MSUB; i++) {
-                    issue_piece(kb1, st ^ 1, i);
+                    load_piece(i);
                     float sa_i;
                     const v8i af = next_af(i, sa_i);
+                    hand_over(i);
 #pragma unroll
                     for (int j = 0; j < NSUB; j++) {
                         const v4f cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -634,6 +649,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                             pend_s[0][2] = sa_i * sbr[j].z;
                             pend_s[0][3] = sa_i * sbr[j].w;
                         }
+                        after_mfma(i, j);
                     }
                 }
 #pragma unroll
@@ -643,9 +659,11 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                         acc[pend_i[l]][pend_j[l]][r] = __builtin_fmaf(pend[l][r], pend_s[l][r], acc[pend_i[l]][pend_j[l]][r]);
             }
         }
-    }
+    };
+    for (int kb = 0; kb + 1 < nkb; kb++) step(kb, fg_bool<true>{});
+    if (nkb > 0) step(nkb - 1, fg_bool<false>{});
 
-    __builtin_amdgcn_s_waitcnt(0);          // the last step's (redundant) staging loads
+    __builtin_amdgcn_s_waitcnt(0);
     if constexpr (POW2) {
         // A scale that is not a positive power of two was applied without its mantissa: the wave's whole
         // output tile becomes NaN, so the misuse shows instead of giving plausible wrong sums.
