@@ -503,10 +503,18 @@ def main():
         yu = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
         yd = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         res = {}
+        # The experts' weights are quantized in one launch each: 128x128 blocks never straddle two experts
+        # (2048 and 7168 are multiples of 128), so W_up [8][2048][7168] quantized as one [16384, 7168] matrix
+        # gives exactly the per-expert codes and scales, in the [E][N/128][K/128] layout.
+        wu2, wuq2, wus2 = wu.view(E * I, H), wuq.view(E * I, H), wus.view(E * I // 128, H // 128)
+        wd2, wdq2, wds2 = wd.view(E * H, I), wdq.view(E * H, I), wds.view(E * H // 128, I // 128)
         for name, fn, flop in [
             ("grouped_up", lambda: fg.fg_fp8_grouped_gemm(xq, sx, wuq, wus, off, y=yu, pow2=POW2), 2.0 * T * I * H),
             ("grouped_down", lambda: fg.fg_fp8_grouped_gemm(hq, sh, wdq, wds, off, y=yd, pow2=POW2), 2.0 * T * I * H),
-            ("quant_moe_x_rowwise", lambda: fg.fg_quantize_act_1x128(xm, q=xq, scales=sx, pow2=POW2), None),
+            ("quant_moe_x_rowwise", lambda: fg.fg_quantize_act_1x128(xm, q=xq, scales=sx, pow2=POW2), ("act", T, H)),
+            ("quant_moe_h_rowwise", lambda: fg.fg_quantize_act_1x128(hm, q=hq, scales=sh, pow2=POW2), ("act", T, I)),
+            ("quant_moe_w_up", lambda: fg.fg_quantize_w_128x128(wu2, q=wuq2, scales=wus2, pow2=POW2), ("w", E * I, H)),
+            ("quant_moe_w_down", lambda: fg.fg_quantize_w_128x128(wd2, q=wdq2, scales=wds2, pow2=POW2), ("w", E * H, I)),
         ]:
             for _ in range(3):
                 fn()
@@ -519,14 +527,17 @@ def main():
                 torch.cuda.synchronize()
                 times.append(e0.elapsed_time(e1))
             ms = float(np.median(times))
-            if flop is not None:
+            if not isinstance(flop, tuple):
                 ach = flop / (ms * 1e-3) / 1e12
                 res[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4)}
             else:
-                gbps = quant_bytes(T, H) / (ms * 1e-3) / 1e9
-                res[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+                kind, rows_, cols_ = flop
+                nbytes = quant_bytes(rows_, cols_) if kind == "act" else quant_w_bytes(rows_, cols_)
+                gbps = nbytes / (ms * 1e-3) / 1e9
+                res[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                             "bytes": nbytes}
         moe = {"workload": "moe_grouped_8experts_65536rows_hidden7168_inter2048", "rows_per_expert": d["rows"].tolist(), **res}
-        del xm, hm, wu, wd, xq, hq, wdq, wds, yu, yd, d
+        del xm, hm, wu, wd, xq, hq, wdq, wds, yu, yd, d, wu2, wuq2, wus2, wd2, wdq2, wds2
 
         # The up-projection's backward on the same expert share (routed rows padded per expert to 128
         # tokens): grouped Dgrad dX = dY . W_up[e] and grouped Wgrad dW_up[e] = dY^T X over each expert's
@@ -539,9 +550,13 @@ def main():
         xq2, sx2, xtq2, sxt2 = fg.fg_quantize_act_1x128_both(xb, pow2=POW2)
         dyq2, sdy2, dytq2, sdyt2 = fg.fg_quantize_act_1x128_both(dyb, pow2=POW2)
         dxb = torch.empty((Tp, H), dtype=f32, device=dev)
+        dxb16 = torch.empty((Tp, H), dtype=torch.bfloat16, device=dev)
         dwb = torch.empty((E, I, H), dtype=f32, device=dev)
         for name, fn, flop in [
             ("grouped_dgrad_up", lambda: fg.fg_fp8_grouped_gemm_dgrad(dyq2, sdy2, wuq, wus, offb, dx=dxb, pow2=POW2),
+             2.0 * Treal * I * H),
+            ("grouped_dgrad_up_bf16_out", lambda: fg.fg_fp8_grouped_gemm_dgrad(dyq2, sdy2, wuq, wus, offb, dx=dxb16,
+                                                                               pow2=POW2),
              2.0 * Treal * I * H),
             ("grouped_wgrad_up", lambda: fg.fg_fp8_grouped_gemm_wgrad(dytq2, sdyt2, xtq2, sxt2, offb, dw=dwb, pow2=POW2),
              2.0 * Treal * I * H),
