@@ -791,23 +791,23 @@ unsigned grid_for(const GemmParams& p, int group) {
 
 // Workgroup shape for one launch: the one with the smaller estimated time, counting full rounds of tiles
 // over the compute units, a tile's work (BM * BN) and the measured per-tile rate of the 8-wave shape
-// relative to the 12-wave one: 11% more MFMA throughput per CU with FP32 scales, 21% with power-of-2
-// scales (measured at the dense-MLP Fprop shape, where the two shapes need 4.5 and 6 rounds).
-// FG_GEMM_TILE=256x192 or 256x256 in the environment forces a shape (tuning and tests).
-bool use_cfg8(const GemmParams& p, int grouped, int pow2) {
+// relative to the 12-wave one: 21% more MFMA throughput per CU (measured at the dense-MLP Fprop shape,
+// where the two shapes need 4.5 and 6 rounds, inside the whole training step: 542 against 580 us with FP32
+// scales, 488 against 553 us with power-of-2 scales). FG_GEMM_TILE=256x192 or 256x256 in the environment
+// forces a shape (tuning and tests).
+bool use_cfg8(const GemmParams& p, int grouped) {
     const char* force = getenv("FG_GEMM_TILE");
     if (force && strcmp(force, "256x256") == 0) return true;
     if (force && strcmp(force, "256x192") == 0) return false;
     const int64_t cus = fg_device_cus();
     const int64_t r12 = (grid_for<Cfg12>(p, grouped) + cus - 1) / cus;
     const int64_t r8 = (grid_for<Cfg8>(p, grouped) + cus - 1) / cus;
-    const double rate8 = pow2 ? 1.21 : 1.11;
-    return (double)r8 * Cfg8::BM * Cfg8::BN / rate8 < (double)r12 * Cfg12::BM * Cfg12::BN;
+    return (double)r8 * Cfg8::BM * Cfg8::BN / 1.21 < (double)r12 * Cfg12::BM * Cfg12::BN;
 }
 
 template <bool B_TRANS, int SBK, int GROUP>
 hipError_t launch(const GemmParams& p, int pow2, hipStream_t stream) {
-    if (use_cfg8(p, GROUP, pow2)) {
+    if (use_cfg8(p, GROUP)) {
         const unsigned grid = grid_for<Cfg8>(p, GROUP);
         return pow2 ? launch_one<Cfg8, B_TRANS, SBK, GROUP, true>(p, grid, stream)
                     : launch_one<Cfg8, B_TRANS, SBK, GROUP, false>(p, grid, stream);
