@@ -2,15 +2,15 @@
 
 One step = the whole hot path over one batch of the DeepSeek-V3-like dense MLP Linear
 (X [4096, 7168], W [18432, 7168], dY [4096, 18432], seeded synthetic bf16):
-  forward : quantize X in both 1x128 tilings (along channels for Fprop, along tokens for Wgrad, one read),
-            quantize W (128x128 blocks), Fprop Y = X W^T (BF16 out)
+  forward : quantize X in both 1x128 tilings (along channels for Fprop, along tokens for Wgrad, one read)
+            and W (128x128 blocks), both in one launch; Fprop Y = X W^T (BF16 out)
   backward: quantize dY in both tilings (one read), Dgrad dX = dY W (FP32 out), Wgrad dW = dY^T X (FP32 out)
 `value` is the FP8 GEMM throughput of the whole step (3 x 2MNK FLOP over the step's wall time), with
 all inputs resident in HBM when the timed region starts. Per-kernel times come from HIP events on the
 stream the kernels run on.
 
-Also reported, beside the headline: the same step with the other scale mode and with one quantizer
-launch per tiling ("variants"), per-kernel roofline fractions, cold-cache quantize bandwidth (a 1 GiB
+Also reported, beside the headline: the same step with the other scale mode, with X's and W's quantizers
+as two launches, and with one quantizer launch per tiling ("variants"), per-kernel roofline fractions, cold-cache quantize bandwidth (a 1 GiB
 read between launches defeats the 256 MB Infinity Cache), the Fprop that quantizes its own output
 against Fprop + quantizer, per-tensor (current and delayed) scaling against the 1x128 tiles, the grouped
 MoE GEMMs on one GPU's expert share, the tiny and accumulation-stress Fprop shapes, the vendor's
@@ -125,11 +125,28 @@ def main():
     )
     B = bufs
 
-    def make_ops(pow2, fused=True):
-        """The step's launches. fused: X and dY are read once each and quantized in both tilings (rows for
-        Fprop/Dgrad, tokens for Wgrad) by fg_quantize_act_1x128_both; otherwise each tiling has its own
-        launch."""
-        if fused:
+    def make_ops(pow2, quant="batched"):
+        """The step's launches. "fused": X and dY are read once each and quantized in both tilings (rows for
+        Fprop/Dgrad, tokens for Wgrad) by fg_quantize_act_1x128_both, W by fg_quantize_w_128x128; "batched":
+        the same, with X's and W's quantization in one launch (fg_quantize_fprop_operands); "separate": each
+        tiling has its own launch."""
+        if quant == "batched":
+            return [
+                ("quant_xw", lambda: fg.fg_quantize_fprop_operands(x, w, pow2=pow2, q_cols=B["xq"], scales_cols=B["sx"],
+                                                                   q_rows=B["xtq"], scales_rows=B["sxt"], qw=B["wq"],
+                                                                   sw=B["sw"]),
+                 "hbm", quant_both_bytes(M, K) + quant_w_bytes(N, K)),
+                ("fprop", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=pow2),
+                 "mfma", 2.0 * M * N * K),
+                ("quant_dy_both", lambda: fg.fg_quantize_act_1x128_both(dy, pow2=pow2, q_cols=B["dyq"], scales_cols=B["sdy"],
+                                                                        q_rows=B["dytq"], scales_rows=B["sdyt"]),
+                 "hbm", quant_both_bytes(M, N)),
+                ("dgrad", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"], pow2=pow2),
+                 "mfma", 2.0 * M * N * K),
+                ("wgrad", lambda: fg.fg_fp8_gemm_wgrad(B["dytq"], B["sdyt"], B["xtq"], B["sxt"], dw=B["dw"], pow2=pow2),
+                 "mfma", 2.0 * M * N * K),
+            ]
+        if quant == "fused":
             return [
                 ("quant_x_both", lambda: fg.fg_quantize_act_1x128_both(x, pow2=pow2, q_cols=B["xq"], scales_cols=B["sx"],
                                                                        q_rows=B["xtq"], scales_rows=B["sxt"]),
@@ -217,31 +234,28 @@ def main():
         return g, ms
 
     POW2 = bool(args.pow2)
-    ops = make_ops(POW2, fused=True)
+    QUANT_DESC = {"batched": "batched quantizers", "fused": "fused quantizers", "separate": "separate quantizers"}
+    ops = make_ops(POW2, "batched")
     ms_eager, per_kernel_ms = measure(ops, args.steps, args.warmup,
-                                      ("pow2" if POW2 else "fp32") + " scales, fused quantizers")
+                                      ("pow2" if POW2 else "fp32") + " scales, batched quantizers")
     # Two more schedules of the same kernels; each one's outputs must equal the sequential step's bit for bit
     # before its time counts:
-    #  - overlapped: a second stream (default priority) runs W's quantizer beside X's and Wgrad beside Dgrad
-    #    (independent kernels: Wgrad's tiles fill Dgrad's last, partial round of workgroups);
+    #  - overlapped: a second stream (default priority) runs Wgrad beside Dgrad (independent kernels: Wgrad's
+    #    tiles fill Dgrad's last, partial round of workgroups);
     #  - the sequential step captured once as a HIP graph and replayed.
     side = torch.cuda.Stream(device=dev)
     by_name = {name: fn for name, fn, _, _ in ops}
 
     def run_step_overlap():
         main = torch.cuda.current_stream(dev)
-        side.wait_stream(main)                      # the previous step's readers of wq / xtq are done
-        with torch.cuda.stream(side):
-            by_name["quant_w_128x128"]()
-        by_name["quant_x_both"]()
-        main.wait_stream(side)
+        by_name["quant_xw"]()
         by_name["fprop"]()
         by_name["quant_dy_both"]()
         side.wait_stream(main)
         with torch.cuda.stream(side):
             by_name["wgrad"]()
         by_name["dgrad"]()
-        main.wait_stream(side)
+        main.wait_stream(side)                      # the next step's X quantizer overwrites what Wgrad reads
 
     def timed(fn, steps, warmup, tag):
         for _ in range(warmup):
@@ -273,7 +287,7 @@ def main():
     if not args.no_overlap:
         ms_overlap = timed(run_step_overlap, args.steps, args.warmup, ("pow2" if POW2 else "fp32") + " scales, overlapped")
         overlap_ok = same_as_eager()
-    graph, ms_graph = measure_graph(ops, args.steps, args.warmup, ("pow2" if POW2 else "fp32") + " scales, fused quantizers")
+    graph, ms_graph = measure_graph(ops, args.steps, args.warmup, ("pow2" if POW2 else "fp32") + " scales, batched quantizers")
     graph_ok = same_as_eager()
     del eager_out, graph
     schedules = {"eager": ms_eager}
@@ -284,24 +298,29 @@ def main():
     launch_mode = min(schedules, key=schedules.get)
     ms_per_step = schedules[launch_mode]
     # Other variants of the same step on the same buffers, reported beside the headline: the other scale
-    # mode, and one launch per tiling instead of the fused quantizers.
+    # mode, X's and W's quantizers as two launches, and one launch per tiling.
     variants = {}
-    sep_ops, sep_per = None, None
-    for pw, fu in ((not POW2, True), (POW2, False), (not POW2, False)):
-        vops = make_ops(pw, fused=fu)
-        vms, vper = measure(vops, args.steps, args.warmup, ("pow2" if pw else "fp32") + " scales, " +
-                            ("fused quantizers" if fu else "separate quantizers"))
-        variants[("pow2" if pw else "fp32") + ("_fused" if fu else "_separate")] = (vops, vms, vper)
-        if pw == POW2 and not fu:
-            sep_ops, sep_per = vops, vper
+    same_mode = {}                                  # variants in the headline's scale mode: their launches
+    for pw, qu in ((not POW2, "batched"), (POW2, "fused"), (not POW2, "fused"), (POW2, "separate"),
+                   (not POW2, "separate")):
+        vops = make_ops(pw, qu)
+        vms, vper = measure(vops, args.steps, args.warmup, ("pow2" if pw else "fp32") + " scales, " + QUANT_DESC[qu])
+        variants[("pow2" if pw else "fp32") + "_" + qu] = (vops, vms, vper)
+        if pw == POW2:
+            same_mode[qu] = (vops, vper)
+    # every quantizer launch of the headline's scale mode, once by name, with its in-step time
+    quant_ops = {}
+    for vops, vper in [(ops, per_kernel_ms)] + [same_mode[q] for q in ("fused", "separate")]:
+        for o in vops:
+            if o[2] == "hbm" and o[0] not in quant_ops:
+                quant_ops[o[0]] = o
+                per_kernel_ms.setdefault(o[0], vper[o[0]])
 
     gemm_flop = 3 * 2.0 * M * N * K
     value = gemm_flop / (ms_per_step * 1e-3) / 1e12
 
     kernels = {}
-    for name, _, bound, work in ops + [o for o in sep_ops if o[2] == "hbm" and o[0] not in per_kernel_ms]:
-        if name not in per_kernel_ms:
-            per_kernel_ms[name] = sep_per[name]
+    for name, _, bound, work in [o for o in ops if o[2] == "mfma"] + list(quant_ops.values()):
         ms = per_kernel_ms[name]
         if bound == "mfma":
             ach = work / (ms * 1e-3) / 1e12
@@ -317,9 +336,7 @@ def main():
     if not args.no_cold:
         scrub = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         sink = torch.empty((), dtype=torch.int32, device=dev)
-        for name, fn, bound, work in ops + [o for o in sep_ops if o[2] == "hbm" and o[0] != "quant_w_128x128"]:
-            if bound != "hbm":
-                continue
+        for name, fn, bound, work in quant_ops.values():
             times = []
             for _ in range(7):
                 torch.amax(scrub, dim=0, out=sink)
@@ -611,7 +628,8 @@ def main():
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": "dsv3_dense_mlp_linear_fwd_bwd", "M_tokens": M, "N_out": N, "K_in": K,
                    "tiles": "1x128 activations, 128x128 weights", "scale_mode": "pow2" if POW2 else "fp32",
-                   "quantizers": "fused (X and dY read once for both tilings)", "accumulate": "fp32, promoted every 128 K",
+                   "quantizers": "batched: X (both tilings, read once) and W in one launch; dY both tilings from one read",
+                   "accumulate": "fp32, promoted every 128 K",
                    "fprop_out": "bf16", "dgrad_out": "f32", "wgrad_out": "f32", "launch": launch_mode},
         "step_ms": {"eager": round(ms_eager, 4), "overlapped": None if ms_overlap is None else round(ms_overlap, 4),
                     "overlapped_matches_eager": overlap_ok,

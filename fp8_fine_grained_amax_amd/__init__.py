@@ -36,6 +36,7 @@ def lib():
         L.fg_quantize_act_1x128.argtypes = [P, I64, I64, I64, I, I, P, P, P]
         L.fg_quantize_w_128x128.argtypes = [P, I64, I64, I64, I, P, P, P]
         L.fg_quantize_act_1x128_both.argtypes = [P, I64, I64, I64, I, P, P, P, P, P]
+        L.fg_quantize_fprop_operands.argtypes = [P, I64, I64, P, I64, I64, I64, I, P, P, P, P, P, P, P]
         L.fg_fp8_gemm_fprop.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
         L.fg_fp8_gemm_fprop_quant.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, I, P]
         L.fg_fp8_gemm_dgrad.argtypes = [P, P, P, P, I64, I64, I64, P, I, I, P]
@@ -49,7 +50,8 @@ def lib():
         L.fg_dequantize_e5m6_1x128.argtypes = [P, P, I64, I64, P, I64, P]
         L.fg_requantize_1x128_to_tokens.argtypes = [P, P, I64, I64, I, P, P, P]
         L.fg_quantize_per_tensor.argtypes = [P, I64, I64, I64, P, I64, I, I, P, P, P, P]
-        for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_w_128x128", "fg_fp8_gemm_fprop",
+        for f in ("fg_quantize_act_1x128", "fg_quantize_act_1x128_both", "fg_quantize_fprop_operands",
+                  "fg_quantize_w_128x128", "fg_fp8_gemm_fprop",
                   "fg_fp8_gemm_fprop_quant", "fg_fp8_gemm_dgrad", "fg_fp8_gemm_wgrad", "fg_fp8_grouped_gemm",
                   "fg_fp8_grouped_gemm_dgrad", "fg_fp8_grouped_gemm_wgrad", "fg_amax_bf16", "fg_quantize_per_tensor",
                   "fg_requantize_1x128_to_tokens", "fg_quantize_e5m6_1x128", "fg_dequantize_e5m6_1x128",
@@ -169,6 +171,39 @@ def fg_quantize_w_128x128(w, pow2: bool = False, q=None, scales=None):
     _check(lib().fg_quantize_w_128x128(_ptr(w), n, k, w.stride(0), FG_SCALE_POW2 if pow2 else FG_SCALE_FP32,
                                        _ptr(q), _ptr(scales), _stream(w.device)), "fg_quantize_w_128x128")
     return q, scales
+
+
+def fg_quantize_fprop_operands(x, w, pow2: bool = False, q_cols=None, scales_cols=None, q_rows=None,
+                               scales_rows=None, qw=None, sw=None):
+    """X [rows, k] in both 1x128 tilings and W [n, k] in 128x128 blocks from one kernel launch: returns
+    (q_cols, scales_cols, q_rows, scales_rows, qw, sw), identical to fg_quantize_act_1x128_both(x) followed
+    by fg_quantize_w_128x128(w)."""
+    _gpu(x, w)
+    for t, what in ((x, "x"), (w, "w")):
+        # an empty tensor is not read, whatever its strides
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
+            raise Fp8fgError(f"{what} must be a 2-D bf16 tensor with unit column stride")
+    rows, k = x.shape
+    n, kw = w.shape
+    if kw != k:
+        raise Fp8fgError(f"x and w must share the contraction width: {k} != {kw}")
+    dev = x.device
+    if q_cols is None:
+        q_cols = torch.empty((rows, k), dtype=torch.uint8, device=dev)
+    if scales_cols is None:
+        scales_cols = torch.empty(((k + 127) // 128, rows), dtype=torch.float32, device=dev)
+    if q_rows is None:
+        q_rows = torch.empty((k, rows), dtype=torch.uint8, device=dev)
+    if scales_rows is None:
+        scales_rows = torch.empty(((rows + 127) // 128, k), dtype=torch.float32, device=dev)
+    if qw is None:
+        qw = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    if sw is None:
+        sw = torch.empty(((n + 127) // 128, (k + 127) // 128), dtype=torch.float32, device=dev)
+    _check(lib().fg_quantize_fprop_operands(_ptr(x), rows, x.stride(0), _ptr(w), n, w.stride(0), k, _mode(pow2),
+                                            _ptr(q_cols), _ptr(scales_cols), _ptr(q_rows), _ptr(scales_rows), _ptr(qw),
+                                            _ptr(sw), _stream(dev)), "fg_quantize_fprop_operands")
+    return q_cols, scales_cols, q_rows, scales_rows, qw, sw
 
 
 def _bf16_2d(x, what):

@@ -21,6 +21,9 @@ hipError_t fg_launch_gemm_grouped_wgrad(const uint8_t* dytq, const float* sdyt, 
                                         int accumulate, int pow2, hipStream_t stream);
 hipError_t fg_launch_quant_act_both(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int pow2,
                                     uint8_t* qc, float* sc, uint8_t* qr, float* sr, hipStream_t stream);
+hipError_t fg_launch_quant_x_both_w(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* qc, float* sc,
+                                    uint8_t* qr, float* sr, const uint16_t* w, int64_t n, int64_t ldw, uint8_t* qw,
+                                    float* sw, int pow2, hipStream_t stream);
 hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
                                 int64_t N, int64_t K, void* y, int out_bf16, int pow2, hipStream_t stream);
 hipError_t fg_launch_gemm_fprop_quant(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
@@ -190,6 +193,30 @@ fg_status fg_quantize_act_1x128_both(const void* x, int64_t rows, int64_t cols, 
     if (cols / 128 > kMaxGridY || rows / 128 > kMaxGridX) return FG_ERR_UNSUPPORTED_SHAPE;
     return from_hip(fg_launch_quant_act_both((const uint16_t*)x, rows, cols, ld_x, mode == FG_SCALE_POW2, q_cols,
                                              scales_cols, q_rows, scales_rows, stream));
+}
+
+fg_status fg_quantize_fprop_operands(const void* x, int64_t rows, int64_t ld_x, const void* w, int64_t n, int64_t ld_w,
+                                     int64_t k, fg_scale_mode mode, uint8_t* q_cols, float* scales_cols,
+                                     uint8_t* q_rows, float* scales_rows, uint8_t* qw, float* sw, hipStream_t stream) {
+    if (rows < 0 || n < 0 || k < 0 || !valid_mode(mode)) return FG_ERR_INVALID_ARG;
+    // a tensor with no rows is not read: its pointers and row stride are ignored
+    if ((rows > 0 && ld_x < k) || (n > 0 && ld_w < k)) return FG_ERR_INVALID_ARG;
+    const bool has_x = rows > 0 && k > 0, has_w = n > 0 && k > 0;
+    if (!has_x && !has_w) return FG_OK;
+    if (has_x && (!x || !q_cols || !scales_cols || !q_rows || !scales_rows)) return FG_ERR_INVALID_ARG;
+    if (has_w && (!w || !qw || !sw)) return FG_ERR_INVALID_ARG;
+    if (rows % 128 != 0 || k % 128 != 0) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (has_x && (!aligned16(x) || !aligned16(q_cols) || !aligned16(q_rows) || !aligned4(scales_cols) ||
+                  !aligned4(scales_rows) || (ld_x % 8) != 0))
+        return FG_ERR_MISALIGNED;
+    if (has_w && (!aligned16(w) || !aligned16(qw) || !aligned4(sw) || (ld_w % 8) != 0)) return FG_ERR_MISALIGNED;
+    // X blocks plus W blocks, one workgroup each, in a one-dimensional grid
+    const int64_t kb = k / 128;
+    const int64_t xb = rows / 128, wb = cdiv(n, 128);
+    if (prod_over(xb + wb, kb, kMaxGridX)) return FG_ERR_UNSUPPORTED_SHAPE;
+    return from_hip(fg_launch_quant_x_both_w((const uint16_t*)x, has_x ? rows : 0, k, ld_x, q_cols, scales_cols, q_rows,
+                                             scales_rows, (const uint16_t*)w, has_w ? n : 0, ld_w, qw, sw,
+                                             mode == FG_SCALE_POW2, stream));
 }
 
 fg_status fg_requantize_1x128_to_tokens(const uint8_t* q_in, const float* s_in, int64_t rows, int64_t cols,

@@ -204,15 +204,16 @@ __global__ __launch_bounds__(256) void fg_quant_act_rows_kernel(const uint16_t* 
 // of the 16 B chunk t%16, so each 16-lane group reads one full 256 B block row. The block max-abs is a
 // register max, a DPP row max, two lane shuffles and a 4-entry LDS exchange; the block is read once.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restrict__ w, int64_t n, int64_t ld,
-                                                         int64_t kblocks, int pow2, uint8_t* __restrict__ q,
-                                                         int64_t ldq, float* __restrict__ scales) {
+// Block (bk, bn): input columns 128 bk.., rows 128 bn...
+__device__ __forceinline__ void fg_quant_w_block(const uint16_t* __restrict__ w, int64_t n, int64_t ld, int64_t kblocks,
+                                                 int pow2, uint8_t* __restrict__ q, int64_t ldq,
+                                                 float* __restrict__ scales, int64_t bk, int64_t bn) {
     __shared__ uint32_t wmax[4];
     const int t = threadIdx.x;
     const int chunk = t & 15;
     const int rsub = t >> 4;
-    const int64_t r0 = (int64_t)blockIdx.y * FG_GROUP;
-    const int64_t c0 = (int64_t)blockIdx.x * FG_GROUP + chunk * 8;
+    const int64_t r0 = bn * FG_GROUP;
+    const int64_t c0 = bk * FG_GROUP + chunk * 8;
 
     uint4 v[8];
 #pragma unroll
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restr
     uint32_t a = wmax[0] > wmax[1] ? wmax[0] : wmax[1];
     uint32_t b = wmax[2] > wmax[3] ? wmax[2] : wmax[3];
     const float s = fg_scale_from_amax_bits(a > b ? a : b, pow2);
-    if (t == 0) scales[blockIdx.y * kblocks + blockIdx.x] = s;
+    if (t == 0) scales[bn * kblocks + bk] = s;
     const fg_divisor d = fg_make_divisor(s, pow2);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -244,6 +245,12 @@ __global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restr
         const uint2 codes = fg_quant8_any(v[i], d, pow2);
         if (r < n) *reinterpret_cast<uint2*>(q + r * ldq + c0) = codes;
     }
+}
+
+__global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restrict__ w, int64_t n, int64_t ld,
+                                                         int64_t kblocks, int pow2, uint8_t* __restrict__ q,
+                                                         int64_t ldq, float* __restrict__ scales) {
+    fg_quant_w_block(w, n, ld, kblocks, pow2, q, ldq, scales, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -256,10 +263,11 @@ __global__ __launch_bounds__(256) void fg_quant_w_kernel(const uint16_t* __restr
 // an LDS transpose buffer [128 columns][128 rows] whose 16 B pieces are XOR-swizzled by column.
 // The bf16 block is read once instead of twice.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fg_quant_act_both_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                                int64_t cols, int64_t ld, int pow2,
-                                                                uint8_t* __restrict__ qc, float* __restrict__ sc,
-                                                                uint8_t* __restrict__ qr, float* __restrict__ sr) {
+// Block (br, bc): rows 128 br.., columns 128 bc...
+__device__ __forceinline__ void fg_quant_act_both_block(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                        int64_t ld, int pow2, uint8_t* __restrict__ qc,
+                                                        float* __restrict__ sc, uint8_t* __restrict__ qr,
+                                                        float* __restrict__ sr, int64_t br, int64_t bc) {
     __shared__ uint32_t colmax[4][64];          // [wave][column pair], packed u16 max-abs
     __shared__ float col_s[128], col_r[128];    // per-column scale and reciprocal
     __shared__ int tiny_w[2];                   // per wave of the column-scale step: a scale below 2^-100
@@ -269,9 +277,9 @@ __global__ __launch_bounds__(256) void fg_quant_act_both_kernel(const uint16_t* 
     const int chunk = t & 15;                   // 8-column chunk within the 128-column block
     const int rgrp = t >> 4;                    // rows 8*rgrp .. 8*rgrp+7 within the 128-row block
     const int wave = t >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * FG_GROUP;
-    const int64_t c0 = (int64_t)blockIdx.y * FG_GROUP;
-    const int64_t g = blockIdx.y;               // column group of the row tiles
+    const int64_t r0 = br * FG_GROUP;
+    const int64_t c0 = bc * FG_GROUP;
+    const int64_t g = bc;                       // column group of the row tiles
 
     uint4 v[8];
 #pragma unroll
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(256) void fg_quant_act_both_kernel(const uint16_t* 
         col_r[c] = d.r;
         const uint64_t tiny = __builtin_amdgcn_ballot_w64(fg_divisor_tiny(d));
         if ((c & 63) == 0) tiny_w[c >> 6] = tiny != 0;
-        sr[(int64_t)blockIdx.x * cols + c0 + c] = s;
+        sr[br * cols + c0 + c] = s;
     }
     __syncthreads();
     const int mode = pow2 ? FG_Q_POW2 : ((tiny_w[0] | tiny_w[1]) ? FG_Q_TINY : FG_Q_FAST);
@@ -358,6 +366,36 @@ __global__ __launch_bounds__(256) void fg_quant_act_both_kernel(const uint16_t* 
         const int c = id >> 3, p = id & 7;
         const uint4 val = codes_t[c * 8 + (p ^ ((c >> 3) & 7))];
         *reinterpret_cast<uint4*>(qr + (c0 + c) * rows + r0 + 16 * p) = val;
+    }
+}
+
+__global__ __launch_bounds__(256) void fg_quant_act_both_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t ld, int pow2,
+                                                                uint8_t* __restrict__ qc, float* __restrict__ sc,
+                                                                uint8_t* __restrict__ qr, float* __restrict__ sr) {
+    fg_quant_act_both_block(x, rows, cols, ld, pow2, qc, sc, qr, sr, blockIdx.x, blockIdx.y);
+}
+
+// ------------------------------------------------------------------------------------------------
+// The Linear operator's two forward operands in one launch: X in both 1x128 tilings and W in 128x128
+// blocks. Workgroups [0, xb) are X blocks (row block fastest, as in fg_quant_act_both_kernel), the rest W
+// blocks (column block fastest, as in fg_quant_w_kernel). One launch streams X and W back to back, so the
+// ramp-up and drain of a launch are paid once for both tensors instead of once each, and the X part no
+// longer runs as a launch too short to reach full HBM bandwidth on its own.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fg_quant_x_both_w_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t ldx, uint8_t* __restrict__ qc,
+                                                                float* __restrict__ sc, uint8_t* __restrict__ qr,
+                                                                float* __restrict__ sr, const uint16_t* __restrict__ w,
+                                                                int64_t n, int64_t ldw, uint8_t* __restrict__ qw,
+                                                                float* __restrict__ sw, int pow2) {
+    const int64_t id = blockIdx.x;
+    const int64_t xrb = rows / FG_GROUP, xb = xrb * (cols / FG_GROUP);
+    if (id < xb) {
+        fg_quant_act_both_block(x, rows, cols, ldx, pow2, qc, sc, qr, sr, id % xrb, id / xrb);
+    } else {
+        const int64_t kb = cols / FG_GROUP, wid = id - xb;
+        fg_quant_w_block(w, n, ldw, kb, pow2, qw, cols, sw, wid % kb, wid / kb);
     }
 }
 
@@ -402,5 +440,14 @@ hipError_t fg_launch_quant_act_both(const uint16_t* x, int64_t rows, int64_t col
                                     uint8_t* qc, float* sc, uint8_t* qr, float* sr, hipStream_t stream) {
     dim3 grid((unsigned)(rows / FG_GROUP), (unsigned)(cols / FG_GROUP));
     hipLaunchKernelGGL(fg_quant_act_both_kernel, grid, dim3(256), 0, stream, x, rows, cols, ld, pow2, qc, sc, qr, sr);
+    return hipGetLastError();
+}
+
+hipError_t fg_launch_quant_x_both_w(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* qc, float* sc,
+                                    uint8_t* qr, float* sr, const uint16_t* w, int64_t n, int64_t ldw, uint8_t* qw,
+                                    float* sw, int pow2, hipStream_t stream) {
+    const int64_t blocks = (rows / FG_GROUP) * (cols / FG_GROUP) + ((n + FG_GROUP - 1) / FG_GROUP) * (cols / FG_GROUP);
+    hipLaunchKernelGGL(fg_quant_x_both_w_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ldx, qc, sc,
+                       qr, sr, w, n, ldw, qw, sw, pow2);
     return hipGetLastError();
 }

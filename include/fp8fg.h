@@ -147,6 +147,22 @@ fg_status fg_requantize_1x128_to_tokens(const uint8_t* q_in, const float* s_in, 
 fg_status fg_quantize_w_128x128(const void* w, int64_t n, int64_t k, int64_t ld_w,
                                 fg_scale_mode mode, uint8_t* q, float* scales, hipStream_t stream);
 
+/* The Linear operator's two forward operands in one launch ([W1]/[W3]/[W4], Figure 6: the Fprop takes X
+ * and W in FP8, and the backward pass keeps X's FP8 tiles for Wgrad; Figure 7 (a): 1x128 activation tiles
+ * and 128x128 weight blocks): writes exactly what fg_quantize_act_1x128_both(x, rows, k, ld_x, mode,
+ * q_cols, scales_cols, q_rows, scales_rows) and fg_quantize_w_128x128(w, n, k, ld_w, mode, qw, sw) write,
+ * bit for bit, from a single kernel launch. Both tensors share the contraction width k.
+ *   x   bf16 [rows][k], row stride ld_x; rows % 128 == 0, k % 128 == 0.
+ *   q_cols u8 [rows][k], scales_cols f32 [k/128][rows]; q_rows u8 [k][rows], scales_rows f32 [rows/128][k].
+ *   w   bf16 [n][k], row stride ld_w; any n >= 0.   qw u8 [n][k], sw f32 [ceil(n/128)][k/128].
+ *   Alignment: x, w, q_cols, q_rows, qw 16-byte aligned; ld_x % 8 == 0, ld_w % 8 == 0; scales 4-byte
+ *   aligned. A tensor with rows == 0 (x) or n == 0 (w) is not read and its pointers and row stride are
+ *   ignored; the launch covers the other one (nothing when both are empty or k == 0).
+ *   FG_ERR_UNSUPPORTED_SHAPE when the two tensors' blocks exceed 2^31 - 1 workgroups in all. */
+fg_status fg_quantize_fprop_operands(const void* x, int64_t rows, int64_t ld_x, const void* w, int64_t n, int64_t ld_w,
+                                     int64_t k, fg_scale_mode mode, uint8_t* q_cols, float* scales_cols,
+                                     uint8_t* q_rows, float* scales_rows, uint8_t* qw, float* sw, hipStream_t stream);
+
 /* Fprop ([W1]/[W3]/[W4]/[W5], Figure 6, forward pass): Y[M][N] = X[M][K] . W[N][K]^T.
  *   xq u8 [M][K], sx f32 [K/128][M]   (from fg_quantize_act_1x128, FG_ALONG_COLS)
  *   wq u8 [N][K], sw f32 [ceil(N/128)][K/128]   (from fg_quantize_w_128x128)

@@ -45,6 +45,9 @@ hipError_t fg_launch_quant_w(const uint16_t*, int64_t n, int64_t k, int64_t ld, 
 }
 hipError_t fg_launch_quant_act_both(const uint16_t*, int64_t rows, int64_t cols, int64_t ld, int pow2, uint8_t*, float*,
                                     uint8_t*, float*, hipStream_t) { return rec("quant_act_both", rows, cols, ld, 0, pow2); }
+hipError_t fg_launch_quant_x_both_w(const uint16_t*, int64_t rows, int64_t cols, int64_t ldx, uint8_t*, float*, uint8_t*,
+                                    float*, const uint16_t*, int64_t n, int64_t ldw, uint8_t*, float*, int pow2,
+                                    hipStream_t) { return rec("quant_x_both_w", rows, cols, ldx, n, pow2, (int)ldw); }
 hipError_t fg_launch_gemm_fprop(const uint8_t*, const float*, const uint8_t*, const float*, int64_t M, int64_t N,
                                 int64_t K, void*, int out_bf16, int pow2, hipStream_t) {
     return rec("gemm_fprop", M, N, K, 0, out_bf16, pow2);
@@ -149,6 +152,29 @@ int main() {
     ACCEPT(fg_quantize_act_1x128_both(P16, 256, 384, 384, FG_SCALE_POW2, U8(P16), F32(P16), U8(P16), F32(P16), 0),
            "quant_act_both");
     CHECK(g_last.v[0] == 256 && g_last.v[1] == 384 && g_last.flags[0] == 1);
+    // X both tilings + W blocks in one launch
+    REJECT(fg_quantize_fprop_operands(P16, 100, 128, P16, 256, 128, 128, FG_SCALE_FP32, U8(P16), F32(P16), U8(P16),
+                                      F32(P16), U8(P16), F32(P16), 0), SHP);
+    REJECT(fg_quantize_fprop_operands(P16, 128, 128, P16, 256, 128, 128, FG_SCALE_FP32, U8(P16), F32(P16), U8(P16),
+                                      F32(P16), U8(PODD), F32(P16), 0), MIS);
+    REJECT(fg_quantize_fprop_operands(P16, 128, 128, nullptr, 256, 128, 128, FG_SCALE_FP32, U8(P16), F32(P16), U8(P16),
+                                      F32(P16), U8(P16), F32(P16), 0), INV);
+    REJECT(fg_quantize_fprop_operands(P16, 128, 128, P16, 256, 120, 128, FG_SCALE_FP32, U8(P16), F32(P16), U8(P16),
+                                      F32(P16), U8(P16), F32(P16), 0), INV);
+    REJECT(fg_quantize_fprop_operands(P16, INT64_MAX - 127, INT64_MAX - 7, P16, INT64_MAX, INT64_MAX - 7, 128, FG_SCALE_FP32,
+                                      U8(P16), F32(P16), U8(P16), F32(P16), U8(P16), F32(P16), 0), SHP);
+    NOOP(fg_quantize_fprop_operands(nullptr, 0, 128, nullptr, 0, 128, 128, FG_SCALE_FP32, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, nullptr, 0));
+    ACCEPT(fg_quantize_fprop_operands(P16, 256, 392, P16, 300, 400, 384, FG_SCALE_POW2, U8(P16), F32(P16), U8(P16),
+                                      F32(P16), U8(P16), F32(P16), 0), "quant_x_both_w");
+    CHECK(g_last.v[0] == 256 && g_last.v[1] == 384 && g_last.v[2] == 392 && g_last.v[3] == 300 &&
+          g_last.flags[0] == 1 && g_last.flags[1] == 400);
+    ACCEPT(fg_quantize_fprop_operands(nullptr, 0, 128, P16, 300, 384, 384, FG_SCALE_FP32, nullptr, nullptr, nullptr,
+                                      nullptr, U8(P16), F32(P16), 0), "quant_x_both_w");
+    CHECK(g_last.v[0] == 0 && g_last.v[3] == 300);
+    ACCEPT(fg_quantize_fprop_operands(P16, 128, 384, nullptr, 0, 384, 384, FG_SCALE_FP32, U8(P16), F32(P16), U8(P16),
+                                      F32(P16), nullptr, nullptr, 0), "quant_x_both_w");
+    CHECK(g_last.v[0] == 128 && g_last.v[3] == 0);
     // requantize
     REJECT(fg_requantize_1x128_to_tokens(U8(P16), F32(P16), 100, 128, FG_SCALE_FP32, U8(P16), F32(P16), 0), SHP);
     REJECT(fg_requantize_1x128_to_tokens(U8(P16), F32(PODD), 128, 128, FG_SCALE_FP32, U8(P16), F32(P16), 0), MIS);

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -69,6 +69,22 @@ def test_quantize_both_rejections(L):
     assert q(A16, 128, 136, 136, 0, A16, A16, A16, A16, None) == SHAPE      # cols % 128
     assert q(A16, 128, 128, 128, 0, A16, A16, ODD, A16, None) == MISALIGNED
     assert q(A16, 0, 128, 128, 0, None, None, None, None, None) == OK        # empty: no-op
+
+
+def test_quantize_fprop_operands_rejections(L):
+    q = L.fg_quantize_fprop_operands
+    out = (A16, A16, A16, A16, A16, A16)
+    assert q(A16, -1, 128, A16, 128, 128, 128, 0, *out, None) == INVALID      # negative rows
+    assert q(A16, 128, 128, A16, 128, 128, 128, 4, *out, None) == INVALID     # bad mode
+    assert q(A16, 128, 64, A16, 128, 128, 128, 0, *out, None) == INVALID      # ld_x < k
+    assert q(A16, 128, 128, A16, 128, 64, 128, 0, *out, None) == INVALID      # ld_w < k
+    assert q(A16, 128, 128, None, 128, 128, 128, 0, *out, None) == INVALID    # null w
+    assert q(A16, 100, 128, A16, 128, 128, 128, 0, *out, None) == SHAPE       # rows % 128
+    assert q(A16, 128, 136, A16, 128, 136, 136, 0, *out, None) == SHAPE       # k % 128
+    assert q(A16, 128, 132, A16, 128, 128, 128, 0, *out, None) == MISALIGNED  # ld_x % 8
+    assert q(A16, 128, 128, ODD, 128, 128, 128, 0, *out, None) == MISALIGNED  # w not 16 B aligned
+    assert q(None, 0, 128, None, 0, 128, 128, 0, *([None] * 6), None) == OK   # empty: no-op
+    assert q(None, 128, 128, None, 128, 128, 0, 0, *([None] * 6), None) == OK  # k == 0: no-op
 
 
 def test_quantize_w_rejections(L):

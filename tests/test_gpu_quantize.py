@@ -290,3 +290,83 @@ def test_both_every_finite_bf16_value(pow2):
     x = finite[:n].reshape(-1, 128)
     xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
     _check_both(xt, pow2)
+
+
+# ------------------------------------------------------------------------------------------------
+# The Linear operator's two forward operands in one launch (fg_quantize_fprop_operands): X in both
+# 1x128 tilings and W in 128x128 blocks, bit-exact against the oracle. Every output buffer starts filled
+# with a sentinel (0x55 codes, NaN scales), so an element the launch never writes cannot pass.
+# ------------------------------------------------------------------------------------------------
+
+def _sentinel_u8(shape):
+    return torch.full(shape, 0x55, dtype=torch.uint8, device="cuda")
+
+
+def _sentinel_f32(shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _padded(t_cpu, ld_pad):
+    t = to_dev(t_cpu)
+    if not ld_pad:
+        return t
+    big = torch.zeros((t.shape[0], t.shape[1] + ld_pad), dtype=torch.bfloat16, device=t.device)
+    big[:, : t.shape[1]] = t
+    return big[:, : t_cpu.shape[1]]
+
+
+def _check_fprop_operands(x_cpu, w_cpu, pow2, ld_pad=0):
+    rows, k = x_cpu.shape
+    n = w_cpu.shape[0]
+    x, w = _padded(x_cpu, ld_pad), _padded(w_cpu, 2 * ld_pad)
+    outs = (_sentinel_u8((rows, k)), _sentinel_f32((k // 128, rows)), _sentinel_u8((k, rows)),
+            _sentinel_f32(((rows + 127) // 128, k)), _sentinel_u8((n, k)), _sentinel_f32(((n + 127) // 128, k // 128)))
+    qc, sc, qr, sr, qw, sw = fg.fg_quantize_fprop_operands(x, w, pow2=pow2, q_cols=outs[0], scales_cols=outs[1],
+                                                           q_rows=outs[2], scales_rows=outs[3], qw=outs[4], sw=outs[5])
+    torch.cuda.synchronize()
+    if rows:
+        xb = bits(x_cpu)
+        for axis, q, s in ((fg.FG_ALONG_COLS, qc, sc), (fg.FG_ALONG_ROWS, qr, sr)):
+            q_ref, s_ref = oracle.quantize_act_1x128(xb, axis, pow2)
+            assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), f"x axis {axis}: scales"
+            bad = np.argwhere(np_u8(q) != q_ref)
+            assert bad.size == 0, f"x axis {axis}: {len(bad)} codes differ, first {bad[:5].tolist()}"
+    else:
+        assert torch.all(qc == 0x55) and torch.all(qr == 0x55), "an empty X must not be written"
+    if n:
+        q_ref, s_ref = oracle.quantize_w_128x128(bits(w_cpu), pow2)
+        assert np.array_equal(sw.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), "w scales differ"
+        bad = np.argwhere(np_u8(qw) != q_ref)
+        assert bad.size == 0, f"w: {len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_fprop_operands_dsv3(dsv3, pow2):
+    """The dense-MLP step's X [4096, 7168] and W [18432, 7168], as the step quantizes them."""
+    x, w, _ = dsv3
+    _check_fprop_operands(x, w, pow2)
+
+
+@pytest.mark.parametrize("rows,n,k,ld_pad", [(128, 128, 128, 0), (256, 300, 384, 8), (384, 1000, 1024, 24),
+                                             (0, 300, 256, 0), (256, 0, 256, 8), (128, 1, 128, 0)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_fprop_operands_shapes(rows, n, k, ld_pad, pow2):
+    """Ragged weight rows, strided inputs, and either tensor empty (its outputs must stay untouched)."""
+    device()
+    rng = np.random.default_rng(rows * 131 + n * 7 + k)
+    x = wl.normal_bf16(rng, (rows, k), 1.0, outlier_channels=min(3, k), outlier_scale=40.0)
+    w = wl.normal_bf16(rng, (n, k), 0.02)
+    _check_fprop_operands(x, w, pow2, ld_pad)
+
+
+def test_fprop_operands_special_values():
+    """Special rows (zeros, signed zeros, subnormals, extremes, ties, tiny scales) in X as rows and as
+    columns, and in W as block rows."""
+    device()
+    t = _special_tiles()
+    a = np.zeros((128, 128), np.uint16)
+    a[: t.shape[0]] = t
+    x = np.concatenate([a, np.ascontiguousarray(a.T)])
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    for pow2 in (False, True):
+        _check_fprop_operands(xt, xt, pow2)
