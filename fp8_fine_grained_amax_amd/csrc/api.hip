@@ -57,6 +57,9 @@ constexpr int64_t kMaxGridX = 2147483647LL;
 constexpr int64_t kMaxGridY = 65535LL;
 constexpr int64_t kMaxGemmTiles = 2147483647LL;
 constexpr int32_t kMaxGroups = 65536;
+// The grouped GEMMs' grid covers the worst-case row tiles (rows / 256 + G) rounded up to a multiple of 32;
+// the host bounds that padded count times the column tiles.
+constexpr int64_t kGroupedRowPad = 31;
 constexpr int64_t kMaxFlatChunks = 1LL << 31;   // per-tensor kernels index 16 B chunks in 32 bits
 // The GEMM kernels address a tile's operand rows with 32-bit offsets from the tile base: up to 255 rows of
 // the contraction length (A, and B stored [N][K]), and up to 128 rows of the output width for the
@@ -295,7 +298,7 @@ fg_status fg_fp8_grouped_gemm(const uint8_t* xq, const float* sx, const uint8_t*
     if (total_rows == 0 || N == 0) return FG_OK;
     if (!y || !d_offsets || (K > 0 && (!xq || !sx || !wq || !sw))) return FG_ERR_INVALID_ARG;
     if (K % 128 != 0 || K > kMaxContraction) return FG_ERR_UNSUPPORTED_SHAPE;
-    if (prod_over(cdiv(total_rows, 256) + G, cdiv(N, 128), kMaxGemmTiles)) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (prod_over(cdiv(total_rows, 256) + G + kGroupedRowPad, cdiv(N, 128), kMaxGemmTiles)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(sx) || !aligned4(sw) || !aligned4(d_offsets))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_grouped(xq, sx, wq, sw, d_offsets, G, total_rows, N, K, y, out == FG_OUT_BF16,
@@ -310,7 +313,7 @@ fg_status fg_fp8_grouped_gemm_dgrad(const uint8_t* dyq, const float* sdy, const 
     if (total_rows == 0 || K == 0) return FG_OK;
     if (!dx || !d_offsets || (N > 0 && (!dyq || !sdy || !wq || !sw))) return FG_ERR_INVALID_ARG;
     if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction || K > kMaxTransposedWidth) return FG_ERR_UNSUPPORTED_SHAPE;
-    if (prod_over(cdiv(total_rows, 256) + G, cdiv(K, 128), kMaxGemmTiles)) return FG_ERR_UNSUPPORTED_SHAPE;
+    if (prod_over(cdiv(total_rows, 256) + G + kGroupedRowPad, cdiv(K, 128), kMaxGemmTiles)) return FG_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(dyq) || !aligned16(wq) || !aligned16(dx) || !aligned4(sdy) || !aligned4(sw) || !aligned4(d_offsets))
         return FG_ERR_MISALIGNED;
     return from_hip(fg_launch_gemm_grouped_dgrad(dyq, sdy, wq, sw, d_offsets, G, total_rows, N, K, dx, out == FG_OUT_BF16,

@@ -19,7 +19,7 @@
 //   256 x 256 x 128,  8 waves (2 x 4) of 128 x 64: 2 waves per SIMD, 128 accumulator VGPRs per wave; a
 //                     wave reads 25% fewer LDS bytes per MFMA, which also lowers the LDS power that
 //                     competes with the matrix cores for the chip's clock.
-// Operand tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging), double-buffered. The
+// Operand tiles go HBM -> LDS with buffer_load_dwordx4 ... lds (no register staging), double-buffered. The
 // next K step's loads are issued in pieces ahead of the current step's first MFMA rows. LDS rows are 16 B-chunk
 // swizzled so fragment reads are bank-conflict-free. The MFMA is issued with the B-role fragment first, so
 // each lane ends up with one output row m and four consecutive output columns n (8 B bf16 / 16 B fp32
@@ -45,6 +45,8 @@
 namespace {
 
 constexpr int BK = 128;
+// Rows of tiles per band of the grouped Fprop's tile order; its grid is a whole number of 8 bands.
+constexpr int GRP_BAND = 4;
 
 template <int WAVES_M_, int WAVES_N_, int WAVE_M_, int WAVE_N_>
 struct TileCfg {
@@ -59,7 +61,7 @@ struct TileCfg {
     static constexpr int SCALES_A = BM * 4, SCALES_B = BN * 4;
     static constexpr int STAGE = STAGE_A + STAGE_B + SCALES_A + SCALES_B;
     static constexpr int LDS_BYTES = 2 * STAGE;
-    // global_load_lds_dwordx4 instructions per stage (1 KB each) and per wave
+    // direct-to-LDS 16-byte load instructions per stage (1 KB each) and per wave
     static constexpr int LA = STAGE_A / 1024, LB = STAGE_B / 1024;
     static constexpr int UA = (LA + NW - 1) / NW, UB = (LB + NW - 1) / NW;
     static constexpr int SLICES_A = BM / 64, SLICES_B = BN / 64;   // 64-float scale slices
@@ -221,15 +223,17 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         SBp += kb0 * N;
         outp = reinterpret_cast<float*>(p.out) + (int64_t)g * p.out_group_stride;
     } else if constexpr (GROUP == GRP_ROWS) {
-        // Grouped Fprop: rows of N tiles are dealt to the XCDs in turn (row k to XCD k % 8), so an XCD keeps
-        // an M tile's N tiles together and the trailing no-op ids of the worst-case grid (a multiple of 8
-        // rows) spread over all XCDs; 3-4% faster on the MoE up-projection. Grouped Dgrad keeps the launch
-        // order, which deals an M tile's N tiles over the XCDs: each XCD then reuses its share of the
-        // transposed weight panel across M tiles (2-3% faster there than dealing whole rows).
+        // Grouped Fprop: bands of GRP_BAND rows of tiles are dealt to the XCDs in turn (band k to XCD k % 8),
+        // and an XCD walks its band column by column, GRP_BAND tiles per column: the tiles it runs at once
+        // form a GRP_BAND x 8 block that shares A and B panels in its L2, and the trailing no-op ids of the
+        // worst-case grid (a multiple of 8 bands) spread over all XCDs. Grouped Dgrad keeps the launch order,
+        // which deals an M tile's N tiles over the XCDs: each XCD then reuses its share of the transposed
+        // weight panel across M tiles (2-3% faster there than dealing whole rows).
         int id = (int)blockIdx.x;
         if constexpr (!B_TRANS) {
             const int b = id, x = b & 7, j = b >> 3;
-            id = ((j / n_tiles) * 8 + x) * n_tiles + j % n_tiles;
+            const int band = j / (GRP_BAND * n_tiles), w = j % (GRP_BAND * n_tiles);
+            id = ((band * 8 + x) * GRP_BAND + w % GRP_BAND) * n_tiles + w / GRP_BAND;
         }
         const int id_m = id / n_tiles;
         const int nt = id % n_tiles;
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     };
 
     // ---------------- global -> LDS load plan (per thread, fixed over K) ----------------
-    // Each global_load_lds_dwordx4 instruction fills 1 KB of LDS: lane l lands at byte 16 l of it.
+    // Each direct-to-LDS 16-byte load instruction fills 1 KB of LDS: lane l lands at byte 16 l of it.
     // A: LA instructions of 8 rows (instruction t: rows 8t .. 8t+7); wave w issues t = w + NW u. A wave
     // with fewer instructions than UA re-issues its previous one (same source, same LDS bytes: harmless),
     // which keeps every wave's issue sequence identical and branch-free.
@@ -784,7 +788,9 @@ template <class C>
 unsigned grid_for(const GemmParams& p, int group) {
     const int64_t n_tiles = (p.N + C::BN - 1) / C::BN;
     const int64_t m_tiles = (p.M + C::BM - 1) / C::BM;
-    if (group == GRP_ROWS) return (unsigned)(((m_tiles + p.G + 7) / 8) * 8 * n_tiles);   // worst case, 8-row multiple
+    // worst case, a whole number of 8 bands of rows (the host bounds it below 2^31 workgroups)
+    constexpr int64_t R = 8 * GRP_BAND;
+    if (group == GRP_ROWS) return (unsigned)(((m_tiles + p.G + R - 1) / R) * R * n_tiles);
     if (group == GRP_K) return (unsigned)(m_tiles * n_tiles * p.G);
     return (unsigned)(m_tiles * n_tiles);
 }

@@ -201,6 +201,13 @@ int main() {
                                FG_SCALE_FP32, 0), SHP);
     REJECT(fg_fp8_grouped_gemm_dgrad(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 8, INT64_MAX, 128, 128, P16,
                                      FG_OUT_F32, FG_SCALE_FP32, 0), SHP);
+    // the grouped grid pads the worst-case row tiles (rows / 256 + G) by up to 31: bounded with the padding
+    REJECT(fg_fp8_grouped_gemm(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 1LL << 34, 128, P16, FG_OUT_BF16,
+                               FG_SCALE_FP32, 0), SHP);
+    ACCEPT(fg_fp8_grouped_gemm(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 1LL << 32, 128, P16, FG_OUT_BF16,
+                               FG_SCALE_FP32, 0), "gemm_grouped");
+    REJECT(fg_fp8_grouped_gemm_dgrad(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 128, 1LL << 34, P16,
+                                     FG_OUT_F32, FG_SCALE_FP32, 0), SHP);
     REJECT(fg_fp8_grouped_gemm_wgrad(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 65536, 128, 1LL << 20, 1LL << 20,
                                      F32(P16), 0, FG_SCALE_FP32, 0), SHP);
     NOOP(fg_fp8_gemm_fprop(nullptr, nullptr, nullptr, nullptr, 0, 128, 128, nullptr, FG_OUT_F32, FG_SCALE_FP32, 0));
