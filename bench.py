@@ -503,6 +503,24 @@ def main():
         del pk, sk, yb
 
     # Grouped MoE GEMM (one GPU's expert share): up-projection then down-projection, BF16 out.
+    def back_to_back_ms(fn, warm=3, groups=5, per_group=10):
+        """Time per launch of `fn` launched back to back, as in a training step: `warm` untimed launches,
+        then `groups` groups of `per_group` launches between two events on the kernels' stream; the median
+        group's time per launch. (A launch timed alone after the device has idled runs several percent
+        slower than in a stream of work.)"""
+        for _ in range(warm):
+            fn()
+        times = []
+        for _ in range(groups):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(per_group):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / per_group)
+        return float(np.median(times))
+
     moe = None
     if not args.no_moe:
         del x, w, dy, bufs, B
@@ -537,17 +555,7 @@ def main():
             ("quant_moe_w_up", lambda: fg.fg_quantize_w_128x128(wu2, q=wuq2, scales=wus2, pow2=POW2), ("w", E * I, H)),
             ("quant_moe_w_down", lambda: fg.fg_quantize_w_128x128(wd2, q=wdq2, scales=wds2, pow2=POW2), ("w", E * H, I)),
         ]:
-            for _ in range(3):
-                fn()
-            times = []
-            for _ in range(10):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1))
-            ms = float(np.median(times))
+            ms = back_to_back_ms(fn)
             if not isinstance(flop, tuple):
                 ach = flop / (ms * 1e-3) / 1e12
                 res[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4)}
@@ -582,17 +590,7 @@ def main():
             ("grouped_wgrad_up", lambda: fg.fg_fp8_grouped_gemm_wgrad(dytq2, sdyt2, xtq2, sxt2, offb, dw=dwb, pow2=POW2),
              2.0 * Treal * I * H),
         ]:
-            for _ in range(3):
-                fn()
-            times = []
-            for _ in range(10):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1))
-            ms = float(np.median(times))
+            ms = back_to_back_ms(fn)
             ach = flop / (ms * 1e-3) / 1e12
             moe[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4)}
         moe["backward_padded_rows"] = Tp

@@ -57,9 +57,9 @@ constexpr int64_t kMaxGridX = 2147483647LL;
 constexpr int64_t kMaxGridY = 65535LL;
 constexpr int64_t kMaxGemmTiles = 2147483647LL;
 constexpr int32_t kMaxGroups = 65536;
-// The grouped GEMMs' grid covers the worst-case row tiles (rows / 256 + G) rounded up to a multiple of 32;
+// The grouped GEMMs' grid covers the worst-case row tiles (rows / 256 + G) rounded up to a multiple of 8;
 // the host bounds that padded count times the column tiles.
-constexpr int64_t kGroupedRowPad = 31;
+constexpr int64_t kGroupedRowPad = 7;
 constexpr int64_t kMaxFlatChunks = 1LL << 31;   // per-tensor kernels index 16 B chunks in 32 bits
 // The GEMM kernels address a tile's operand rows with 32-bit offsets from the tile base: up to 255 rows of
 // the contraction length (A, and B stored [N][K]), and up to 128 rows of the output width for the

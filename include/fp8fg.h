@@ -56,7 +56,7 @@
  * Size limits of every GEMM (the kernels address operand rows with 32-bit offsets from the tile base):
  * the contraction length is at most 2^24, and Dgrad's output width (its K) at most 2^25. A launch has at
  * most 2^31 - 1 workgroups: a GEMM with more than 2^31 - 1 tiles of 256 x 128 outputs, or a grouped GEMM
- * with more than 2^31 - 1 in (total_rows / 256 + G + 31) x (output width / 128), is refused. Larger shapes
+ * with more than 2^31 - 1 in (total_rows / 256 + G + 7) x (output width / 128), is refused. Larger shapes
  * return FG_ERR_UNSUPPORTED_SHAPE.
  *
  * Every GEMM picks one of two workgroup tiles per launch (256x192 or 256x256 outputs) from the problem size

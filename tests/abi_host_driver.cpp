@@ -201,10 +201,11 @@ int main() {
                                FG_SCALE_FP32, 0), SHP);
     REJECT(fg_fp8_grouped_gemm_dgrad(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 8, INT64_MAX, 128, 128, P16,
                                      FG_OUT_F32, FG_SCALE_FP32, 0), SHP);
-    // the grouped grid pads the worst-case row tiles (rows / 256 + G) by up to 31: bounded with the padding
-    REJECT(fg_fp8_grouped_gemm(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 1LL << 34, 128, P16, FG_OUT_BF16,
+    // the grouped grid pads the worst-case row tiles (rows / 256 + G) by up to 7: bounded with the padding
+    // ((2 + 7) x 2^28 > 2^31 - 1 although 2 x 2^28 is not)
+    REJECT(fg_fp8_grouped_gemm(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 1LL << 35, 128, P16, FG_OUT_BF16,
                                FG_SCALE_FP32, 0), SHP);
-    ACCEPT(fg_fp8_grouped_gemm(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 1LL << 32, 128, P16, FG_OUT_BF16,
+    ACCEPT(fg_fp8_grouped_gemm(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 1LL << 34, 128, P16, FG_OUT_BF16,
                                FG_SCALE_FP32, 0), "gemm_grouped");
     REJECT(fg_fp8_grouped_gemm_dgrad(U8(P16), F32(P16), U8(P16), F32(P16), I32(P16B), 1, 256, 128, 1LL << 34, P16,
                                      FG_OUT_F32, FG_SCALE_FP32, 0), SHP);
