@@ -1,7 +1,8 @@
 """The fine-grained FP8 Linear step captured in a HIP graph: every replay must reproduce the eager step
 bit for bit (all kernels are deterministic), with the program's own eager work and synchronisations
-between replays. The step is the benchmark's: X and dY quantized in both 1x128 tilings, W in 128x128
-blocks, Fprop (BF16 out), Dgrad and Wgrad (FP32 out), at a shape of several tiles with ragged edges.
+between replays. The step is the benchmark's: X in both 1x128 tilings and W in 128x128 blocks from one
+launch, dY in both tilings, Fprop (BF16 out), Dgrad and Wgrad (FP32 out), at a shape of several tiles with
+ragged edges.
 """
 import numpy as np
 import pytest
@@ -15,8 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _step(x, w, dy, pow2):
-    xq, sx, xtq, sxt = fg.fg_quantize_act_1x128_both(x, pow2=pow2)
-    wq, sw = fg.fg_quantize_w_128x128(w, pow2=pow2)
+    xq, sx, xtq, sxt, wq, sw = fg.fg_quantize_fprop_operands(x, w, pow2=pow2)
     y = fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, pow2=pow2)
     dyq, sdy, dytq, sdyt = fg.fg_quantize_act_1x128_both(dy, pow2=pow2)
     dx = fg.fg_fp8_gemm_dgrad(dyq, sdy, wq, sw, pow2=pow2)
@@ -68,6 +68,8 @@ def test_every_entry_point_in_one_graph():
     f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
     o = {"xq": u8(M, K), "sx": f32(K // 128, M), "xtq": u8(K, M), "sxt": f32(M // 128, K),
          "xq2": u8(M, K), "sx2": f32(K // 128, M), "xtq2": u8(K, M), "sxt2": f32(M // 128, K),
+         "xq3": u8(M, K), "sx3": f32(K // 128, M), "xtq3": u8(K, M), "sxt3": f32(M // 128, K),
+         "wq3": u8(N, K), "sw3": f32(N // 128, K // 128),
          "wq": u8(N, K), "sw": f32(N // 128, K // 128), "wgq": u8(2, N, K), "swg": f32(2, N // 128, K // 128),
          "dyq": u8(M, N), "sdy": f32(N // 128, M), "dytq": u8(N, M), "sdyt": f32(M // 128, N),
          "rq": u8(K, M), "rs": f32(M // 128, K), "e5": u8(M, K * 3 // 2), "e5s": f32(K // 128, M),
@@ -82,6 +84,8 @@ def test_every_entry_point_in_one_graph():
         fg.fg_quantize_act_1x128(x, axis=fg.FG_ALONG_ROWS, q=o["xtq"], scales=o["sxt"])
         fg.fg_quantize_act_1x128_both(x, q_cols=o["xq2"], scales_cols=o["sx2"], q_rows=o["xtq2"], scales_rows=o["sxt2"])
         fg.fg_quantize_w_128x128(w, q=o["wq"], scales=o["sw"])
+        fg.fg_quantize_fprop_operands(x, w, q_cols=o["xq3"], scales_cols=o["sx3"], q_rows=o["xtq3"],
+                                      scales_rows=o["sxt3"], qw=o["wq3"], sw=o["sw3"])
         for g in range(2):
             fg.fg_quantize_w_128x128(wg[g * N:(g + 1) * N], q=o["wgq"][g], scales=o["swg"][g])
         fg.fg_quantize_act_1x128_both(dy, q_cols=o["dyq"], scales_cols=o["sdy"], q_rows=o["dytq"], scales_rows=o["sdyt"])
