@@ -457,9 +457,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     // wave of the SIMD waiting on LDS. The 128x128 block scale of step kb+1 is fetched one step ahead.
     float sb_next = 1.0f;
     uint32_t bad_scale = 0;                 // power-of-2 mode: sign or mantissa bits seen in any scale
-    // Two A register sets fit wherever the promotion leaves 8 registers free; the FP32-scale Wgrad
-    // (per-row B scales) and the 256x256 FP32-scale Fprop read each row's fragment just before it.
-    constexpr bool AF_AHEAD = POW2 || SBK == SB_BLOCK_T || (C::NW == 12 && SBK == SB_BLOCK);
+    // Two A register sets fit wherever the promotion leaves 8 registers free; the FP32-scale Wgrad (per-row
+    // B scales, two scale products per element) reads each row's fragment just before it.
+    constexpr bool AF_AHEAD = POW2 || SBK != SB_ROW;
     v8i bf[NSUB];                           // B-role fragments of the wave's NSUB N tiles, one K step
     float4 sbr[NSUB];                       // per-row B scales (FP32 mode) of the lane's 4 output columns
     int ebr[NSUB];                          // per-row B scales (power-of-2 mode) as E8M0, column lrow
@@ -571,8 +571,11 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         } else {
             // VALU promotion, software-pipelined so that no FMA reads the result of the MFMA issued just
             // before it (a VALU read of an MFMA result waits for the whole MFMA). With registers to spare
-            // (8-wave shape, one scale per lane) the FMAs that fold row i-1 into the FP32 accumulators
-            // follow the MFMAs of row i; otherwise the FMAs of each tile follow the next tile's MFMA.
+            // (8-wave shape, one scale per lane) the FMAs that fold row i-1 into the FP32 accumulators go
+            // with the MFMAs of row i, four after each MFMA, so that the wave's own VALU work runs while its
+            // MFMAs execute; the wave keeps its raised priority through the FMAs (measured 2-3% faster on
+            // the FP32-scale Fprop and Dgrad than issuing the row's MFMAs first and its FMAs after); otherwise
+            // the FMAs of each tile follow the next tile's MFMA.
             constexpr bool ROW_PIPE = C::NW == 8 && SBK != SB_ROW;
             if constexpr (ROW_PIPE) {
                 v4f prev[NSUB], cur[NSUB];
@@ -591,7 +594,6 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                                                                                      0, 0, 0, 127, 0, 127);
                             after_mfma(i, j);
                         }
-                        if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
                     }
                     if (i > 0) {
                         const float s = sa_prev * sb_blk;
@@ -599,6 +601,17 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                         for (int j = 0; j < NSUB; j++)
 #pragma unroll
                             for (int r = 0; r < 4; r++) acc[i - 1][j][r] = __builtin_fmaf(prev[j][r], s, acc[i - 1][j][r]);
+                    }
+                    // the interleave (not in the hand-over row, whose MFMAs sit behind scheduling fences)
+                    if (i > 0 && i < MSUB - 1) {
+#pragma unroll
+                        for (int j = 0; j < NSUB; j++) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU operations
+                        }
+                    }
+                    if (i < MSUB) {
+                        if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
                     }
 #pragma unroll
                     for (int j = 0; j < NSUB; j++) prev[j] = cur[j];
