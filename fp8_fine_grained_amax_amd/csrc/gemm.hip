@@ -621,8 +621,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                 // Tile-lagged promotion: the FMAs issued after MFMA t fold tile t - LAG, whose result is long
                 // complete. Per-row B scales (two scale products per element) take the deeper lag where the
                 // registers allow it (8-wave shape); measured 3-4% faster on Wgrad than folding tile t - 1,
-                // and neutral on the 256x192 Fprop.
-                constexpr int LAG = SBK == SB_ROW && C::NW == 8 ? 3 : 2;
+                // and neutral on the 256x192 Fprop. The 12-wave shape's Wgrad (168 VGPRs per wave) folds
+                // tile t - 1: one more pending tile there spills registers to scratch.
+                constexpr int LAG = SBK != SB_ROW ? 2 : C::NW == 8 ? 3 : 1;
                 v4f pend[LAG];
                 float pend_s[LAG][4];
                 int pend_i[LAG], pend_j[LAG];
