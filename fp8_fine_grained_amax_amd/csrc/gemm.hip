@@ -754,6 +754,73 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
         }
         return;
     }
+    if constexpr (NW == 8 && WAVE_M == 128 && WAVE_N == 64 && C::LDS_BYTES >= NW * 64 * 256) {
+        // FP32 output through LDS. In the MFMA layout one 16-byte store per lane writes 16 rows x 64 B, and
+        // a compute unit streams such stores at about a third of the rate of stores that write 4 rows x
+        // 256 B. Each wave re-lays half of its 128x64 tile (64 rows x 256 B) in a private 16 KB LDS region
+        // (16-byte chunk c of row r at c ^ (r % 16): conflict-free for the writes, whose 16 lanes share a
+        // chunk and span 16 rows, and for the reads, whose 16 lanes share a row) and stores it 4 rows x
+        // 256 B at a time. The values are only moved. The condition is uniform over the workgroup, so every
+        // wave reaches the barrier that frees the stages (the last K step's fragment reads are then done).
+        // BF16 output: the wave's whole tile (128 rows x 128 B) fits its region; the MFMA layout's 8-byte
+        // stores write 16 rows x 32 B, the staged ones 8 full 128 B rows (16-byte chunk c of row r at
+        // c ^ ((r / 2) % 8): rows r, r + 1 share a 256 B bank window, so 16 rows of one chunk, or two rows
+        // of 8 chunks, cover its 16 chunk slots once).
+        if (p.out_bf16 && (N & 7) == 0) {
+            __syncthreads();
+            if (wave_n0 + WAVE_N <= N) {
+                uint8_t* reg = smem + wave * (128 * 128);
+                uint16_t* o = reinterpret_cast<uint16_t*>(outp);
+#pragma unroll
+                for (int i = 0; i < MSUB; i++)
+#pragma unroll
+                    for (int j = 0; j < NSUB; j++) {
+                        const int r = i * 16 + lrow;
+                        const int c = (2 * j + (lane >> 5)) ^ ((r >> 1) & 7);
+                        uint2 v;
+                        v.x = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
+                        v.y = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
+                        *reinterpret_cast<uint2*>(reg + r * 128 + c * 16 + ((lane >> 4) & 1) * 8) = v;
+                    }
+#pragma unroll
+                for (int k = 0; k < 16; k++) {
+                    const int r = 8 * k + (lane >> 3);
+                    const int c = lane & 7;
+                    const uint4 v = *reinterpret_cast<const uint4*>(reg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+                    const int64_t m = m0 + wm * WAVE_M + r;
+                    if (m < m_end) *reinterpret_cast<uint4*>(o + m * N + wave_n0 + c * 8) = v;
+                }
+                return;
+            }
+        } else if (!p.out_bf16 && vec_ok) {
+            __syncthreads();
+            if (wave_n0 + WAVE_N <= N) {
+                uint8_t* reg = smem + wave * (64 * 256);
+                float* o = reinterpret_cast<float*>(outp);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+#pragma unroll
+                        for (int j = 0; j < NSUB; j++) {
+                            const int r = i * 16 + lrow;
+                            const int c = (j * 4 + (lane >> 4)) ^ lrow;
+                            *reinterpret_cast<v4f*>(reg + r * 256 + c * 16) = acc[h * 4 + i][j];
+                        }
+#pragma unroll
+                    for (int k = 0; k < 16; k++) {
+                        const int r = 4 * k + (lane >> 4);
+                        const int c = lane & 15;
+                        const v4f v = *reinterpret_cast<const v4f*>(reg + r * 256 + ((c ^ (r & 15)) << 4));
+                        const int64_t m = m0 + wm * WAVE_M + h * 64 + r;
+                        if (m < m_end)
+                            *reinterpret_cast<float4*>(o + m * N + wave_n0 + c * 4) = make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                }
+                return;
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < MSUB; i++) {
         const int64_t m = m0 + wm * WAVE_M + i * 16 + lrow;
