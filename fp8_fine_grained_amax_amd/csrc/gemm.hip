@@ -719,6 +719,12 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
             if (lane < 16) rmax[wn * BM + wm * WAVE_M + i * 16 + lrow] = mx;
         }
         __syncthreads();
+        // With the whole 256-column tile inside the output (uniform over the workgroup), the codes go
+        // through an LDS copy of the tile ([BM][BN B], 16-byte chunk c of row r at c ^ (r % 16)) and every
+        // wave stores BM / NW full rows, 4 rows x 256 B per instruction, instead of 16 rows x 16 B from the
+        // MFMA layout.
+        const bool staged = n0 + BN <= N;
+        uint8_t* ctile = smem + C::WAVES_N * BM * 4;
 #pragma unroll
         for (int i = 0; i < MSUB; i++) {
             const int row = wm * WAVE_M + i * 16 + lrow;
@@ -748,9 +754,26 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                     c = fg_cvt2q<FG_Q_TINY, true>(fg_bf16_lo(hi), fg_bf16_hi(hi), d, c);
                 }
                 const int64_t n = wave_n0 + j * 16 + lcol4;
-                if (row_ok && n < N) *reinterpret_cast<uint32_t*>(p.q_out + m * N + n) = c;
+                if (staged) {
+                    const int ch = (wn * (WAVE_N / 16) + j) ^ lrow;
+                    *reinterpret_cast<uint32_t*>(ctile + row * BN + ch * 16 + lcol4) = c;
+                } else if (row_ok && n < N) {
+                    *reinterpret_cast<uint32_t*>(p.q_out + m * N + n) = c;
+                }
             }
             if ((wn & 1) == 0 && lane < 16 && row_ok && wave_n0 < N) p.s_out[(wave_n0 >> 7) * p.M + m] = sc;
+        }
+        if (staged) {
+            static_assert(BN == 256 && BM % (4 * NW) == 0, "staged code rows: 16 lanes x 16 B per row");
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < BM / (4 * NW); k++) {
+                const int r = wave * (BM / NW) + 4 * k + (lane >> 4);
+                const int ch = lane & 15;
+                const uint4 v = *reinterpret_cast<const uint4*>(ctile + r * BN + ((ch ^ (r & 15)) << 4));
+                const int64_t m = m0 + r;
+                if (m < m_end) *reinterpret_cast<uint4*>(p.q_out + m * N + n0 + ch * 16) = v;
+            }
         }
         return;
     }
