@@ -38,7 +38,9 @@ def _kernel_metadata(obj):
         notes = subprocess.run([f"{LLVM}/llvm-readelf", "--notes", co], check=True, capture_output=True,
                                text=True).stdout
     out = []
-    for block in notes.split("  - .")[1:]:
+    # one top-level list entry per kernel ("  - ." at the start of a line); the argument lists nested in
+    # each entry are indented further
+    for block in re.split(r"^  - \.", notes, flags=re.M)[1:]:
         name = re.search(r"\.name:\s+(\S+)", block)
         if not name or not name.group(1).startswith("_Z"):
             continue
