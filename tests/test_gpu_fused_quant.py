@@ -20,7 +20,7 @@ from tests.gpu_util import TOL_BF16, bf16_bits_to_f64, bits, device, normwise, n
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1, 128, 128), (130, 128, 256), (300, 512, 384), (1000, 768, 512), (256, 2304, 1024)]
+SHAPES = [(1, 128, 128), (130, 128, 256), (300, 512, 384), (200, 640, 256), (1000, 768, 512), (256, 2304, 1024)]
 MODES = [(False, False), (True, True), (False, True), (True, False)]   # (operand scales, output scales)
 
 
