@@ -22,8 +22,10 @@
 // Operand tiles go HBM -> LDS with buffer_load_dwordx4 ... lds (no register staging), double-buffered. The
 // next K step's loads are issued in pieces ahead of the current step's first MFMA rows. LDS rows are 16 B-chunk
 // swizzled so fragment reads are bank-conflict-free. The MFMA is issued with the B-role fragment first, so
-// each lane ends up with one output row m and four consecutive output columns n (8 B bf16 / 16 B fp32
-// stores).
+// each lane ends up with one output row m and four consecutive output columns n. The 256 x 256 shape
+// re-lays each wave's finished tile in LDS and stores it in full rows (a compute unit streams 16-row x
+// 64-byte stores at a third of the rate of full-row ones); the 256 x 192 shape and tiles that run past N
+// store straight from that layout (8 B bf16 / 16 B fp32 per lane).
 //
 // Variants:
 //   B_TRANS   B is stored [K][N] (the weight W[N_contr][K_out] read by Dgrad): the tile lands in LDS as
