@@ -23,6 +23,7 @@ The headline uses fp32 scales (amax/448); --pow2 makes power-of-2 scales the hea
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -37,10 +38,19 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
+def code_text(src):
+    """Source text without its comments and with whitespace runs collapsed: what the compiler sees."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash():
+    """Identifies the kernels' code (comments and layout excluded): the HBM counters in
+    profiles/traffic_counters.json are used only for the code they were taken on."""
     h = hashlib.sha256()
     for f in ("gemm.hip", "quant.hip", "common.h"):
-        h.update(open(os.path.join(ROOT, "fp8_fine_grained_amax_amd", "csrc", f), "rb").read())
+        h.update(code_text(open(os.path.join(ROOT, "fp8_fine_grained_amax_amd", "csrc", f)).read()).encode())
     return h.hexdigest()[:16]
 
 
