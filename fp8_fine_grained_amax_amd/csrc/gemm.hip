@@ -838,8 +838,17 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                         const int c = lane & 15;
                         const v4f v = *reinterpret_cast<const v4f*>(reg + r * 256 + ((c ^ (r & 15)) << 4));
                         const int64_t m = m0 + wm * WAVE_M + h * 64 + r;
-                        if (m < m_end)
-                            *reinterpret_cast<float4*>(o + m * N + wave_n0 + c * 4) = make_float4(v[0], v[1], v[2], v[3]);
+                        if (m < m_end) {
+                            // A weight gradient goes to the optimizer, not to the next kernel: streamed
+                            // past the caches, its 528 MB (dense-MLP shape) leave no dirty lines whose
+                            // write-back the next HBM-bound kernel would pay for (the next X + W quantizer
+                            // then ran in 98 instead of 121 us, Wgrad itself unchanged). Other outputs
+                            // are usually read next and stay cached.
+                            if constexpr (SBK == SB_ROW)
+                                __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(o + m * N + wave_n0 + c * 4));
+                            else
+                                *reinterpret_cast<float4*>(o + m * N + wave_n0 + c * 4) = make_float4(v[0], v[1], v[2], v[3]);
+                        }
                     }
                 }
                 return;
