@@ -380,10 +380,12 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     // loads spread out disturb the MFMA stream less). Measured per kernel on the dense-MLP and MoE GEMMs
     // (same box, each against its neighbours): 256x192: F = 2. 256x256: the FP32-scale Fprop, whose
     // interleaved promotion keeps the VALU busy between MFMAs, F = 4 (2-4% faster than 3, dense and
-    // grouped); the other 128x128-block kernels F = 3; the FP32-scale Wgrad spreads them over every row but
-    // the last (the loads must be out before the step's hand-over barrier), the power-of-2 Wgrad F = 3 (5%
-    // faster than spreading).
-    constexpr int F = C::NW == 12 ? 2 : SBK == SB_ROW ? (POW2 ? 3 : MSUB - 1) : (!B_TRANS && !POW2 ? 4 : 3);
+    // grouped) and the FP32-scale grouped Dgrad (1% faster); the other 128x128-block kernels F = 3; the
+    // FP32-scale Wgrad spreads them over every row but the last (the loads must be out before the step's
+    // hand-over barrier), the power-of-2 Wgrad F = 3 (5% faster than spreading).
+    constexpr int F = C::NW == 12 ? 2
+                    : SBK == SB_ROW ? (POW2 ? 3 : MSUB - 1)
+                    : (!POW2 && (!B_TRANS || GROUP == GRP_ROWS)) ? 4 : 3;
     static_assert(F <= MSUB - 1, "the next stage's loads are all issued before the last row's hand-over barrier");
     // A wave raises its priority while it issues a row of MFMAs, so the SIMD keeps the matrix core fed
     // ahead of the other waves' loads and LDS reads (measured inside the training step: Fprop 2-3% faster,
