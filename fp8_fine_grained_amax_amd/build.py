@@ -51,5 +51,23 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+C_CONSUMER = os.path.join(ROOT, "tests", "c_consumer")
+
+
+def build_c_consumer(verbose: bool = False) -> str:
+    """tests/c_consumer: a C++ program that calls the library through include/fp8fg.h only (the GPU test
+    tests/test_gpu_c_consumer.py runs it); linked against libfp8fg.so in this package directory."""
+    cmd = [HIPCC, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_consumer.cpp"),
+           "-L", HERE, "-lfp8fg", "-Wl,-rpath,$ORIGIN/../fp8_fine_grained_amax_amd", "-o", C_CONSUMER + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr + "\n")
+        raise RuntimeError("hipcc failed on tests/c_consumer.cpp")
+    os.replace(C_CONSUMER + ".tmp", C_CONSUMER)
+    return C_CONSUMER
+
+
 if __name__ == "__main__":
     print(build(verbose=True, extra=sys.argv[1:]))
