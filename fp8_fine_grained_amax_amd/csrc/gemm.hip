@@ -175,7 +175,10 @@ __device__ __forceinline__ int e8m0_of(float s, uint32_t& bad) {
     return (int)(u >> 23) & 0xFF;
 }
 
-template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE>
+// STREAM: the output tile is stored past the caches (chosen per launch, see launch()); a compile-time
+// choice because the compiler folds a run-time choice between an ordinary and a non-temporal store of the
+// same value into one ordinary store.
+template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE, bool STREAM = false>
 __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     constexpr int BM = C::BM, BN = C::BN, NW = C::NW, MSUB = C::MSUB, NSUB = C::NSUB;
     constexpr int WAVE_M = C::WAVE_M, WAVE_N = C::WAVE_N;
@@ -818,7 +821,12 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                     const int c = lane & 7;
                     const uint4 v = *reinterpret_cast<const uint4*>(reg + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
                     const int64_t m = m0 + wm * WAVE_M + r;
-                    if (m < m_end) *reinterpret_cast<uint4*>(o + m * N + wave_n0 + c * 8) = v;
+                    if (m < m_end) {
+                        if constexpr (STREAM)   // an output too large to stay cached (see launch())
+                            __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(o + m * N + wave_n0 + c * 8));
+                        else
+                            *reinterpret_cast<uint4*>(o + m * N + wave_n0 + c * 8) = v;
+                    }
                 }
                 return;
             }
@@ -844,12 +852,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
                         const v4f v = *reinterpret_cast<const v4f*>(reg + r * 256 + ((c ^ (r & 15)) << 4));
                         const int64_t m = m0 + wm * WAVE_M + h * 64 + r;
                         if (m < m_end) {
-                            // A weight gradient goes to the optimizer, not to the next kernel: streamed
-                            // past the caches, its 528 MB (dense-MLP shape) leave no dirty lines whose
-                            // write-back the next HBM-bound kernel would pay for (the next X + W quantizer
-                            // then ran in 98 instead of 121 us, Wgrad itself unchanged). Other outputs
-                            // are usually read next and stay cached.
-                            if constexpr (SBK == SB_ROW)
+                            // Streamed past the caches: weight gradients (they go to the optimizer, not
+                            // to the next kernel) and outputs too large to stay cached (see launch()).
+                            if constexpr (SBK == SB_ROW || STREAM)
                                 __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(o + m * N + wave_n0 + c * 4));
                             else
                                 *reinterpret_cast<float4*>(o + m * N + wave_n0 + c * 4) = make_float4(v[0], v[1], v[2], v[3]);
@@ -893,9 +898,9 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     }
 }
 
-template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE>
+template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE, bool STREAM = false>
 hipError_t launch_one(const GemmParams& p, unsigned grid, hipStream_t stream) {
-    auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUP, POW2, EPI>;
+    auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUP, POW2, EPI, STREAM>;
     static std::atomic<uint64_t> lds_limit_set{0};
     const hipError_t e = fg_set_lds_limit_once((const void*)kern, C::LDS_BYTES, lds_limit_set);
     if (e != hipSuccess) return e;
@@ -929,9 +934,26 @@ bool use_cfg8(const GemmParams& p, int grouped) {
     return (double)r8 * Cfg8::BM * Cfg8::BN / 1.21 < (double)r12 * Cfg12::BM * Cfg12::BN;
 }
 
+// An output at least as large as the 256 MB Infinity Cache cannot stay there for the next kernel: its
+// stores go past the caches instead of filling them with dirty lines that the next kernels would pay to
+// write back, and that would evict the operands this kernel re-reads. Measured with back-to-back launches of
+// the MoE share (same box, outputs bit-identical): grouped Dgrad (1.9 GB of FP32 dX) 1159 -> 1046 us,
+// down-projection (940 MB of BF16) 1015 -> 973 us, up-projection (268 MB) 953 -> 945 us. The dense-MLP Fprop
+// and Dgrad outputs (151 and 117 MB) keep ordinary stores: the next layer reads them, from the cache if
+// still there.
+constexpr int64_t kStreamOutBytes = 256ll << 20;
+
 template <bool B_TRANS, int SBK, int GROUP>
 hipError_t launch(const GemmParams& p, int pow2, hipStream_t stream) {
     if (use_cfg8(p, GROUP)) {
+        if constexpr (SBK != SB_ROW) {   // weight gradients are always streamed
+            const int64_t out_bytes = p.M * p.N * (p.out_bf16 ? 2 : 4);
+            if (out_bytes >= kStreamOutBytes) {
+                const unsigned grid = grid_for<Cfg8>(p, GROUP);
+                return pow2 ? launch_one<Cfg8, B_TRANS, SBK, GROUP, true, EPI_STORE, true>(p, grid, stream)
+                            : launch_one<Cfg8, B_TRANS, SBK, GROUP, false, EPI_STORE, true>(p, grid, stream);
+            }
+        }
         const unsigned grid = grid_for<Cfg8>(p, GROUP);
         return pow2 ? launch_one<Cfg8, B_TRANS, SBK, GROUP, true>(p, grid, stream)
                     : launch_one<Cfg8, B_TRANS, SBK, GROUP, false>(p, grid, stream);
