@@ -13,7 +13,8 @@ Also reported, beside the headline: the same step with the other scale mode, wit
 as two launches, and with one quantizer launch per tiling ("variants"), per-kernel roofline fractions, cold-cache quantize bandwidth (a 1 GiB
 read between launches defeats the 256 MB Infinity Cache), the Fprop that quantizes its own output
 against Fprop + quantizer, per-tensor (current and delayed) scaling against the 1x128 tiles, the grouped
-MoE GEMMs on one GPU's expert share, the tiny and accumulation-stress Fprop shapes, the vendor's
+MoE GEMMs on one GPU's expert share, the tiny and accumulation-stress Fprop shapes, Fprop and Dgrad
+over whole rounds of output tiles against the step's partly filled last round, the vendor's
 per-tensor FP8 GEMM at the Fprop shape, and the CPU oracle timed on a bounded sample of the workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pow2] [--no-moe] [--no-cpu] [--no-cold]
@@ -80,7 +81,7 @@ def main():
     ap.add_argument("--no-vendor", action="store_true")
     ap.add_argument("--no-fused-epilogue", action="store_true")
     ap.add_argument("--no-per-tensor", action="store_true")
-    ap.add_argument("--no-small", action="store_true", help="skip the tiny and accumulation-stress timings")
+    ap.add_argument("--no-small", action="store_true", help="skip the tiny, accumulation-stress and tile-round timings")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the two-stream schedule (a profile's per-kernel means then hold sequential launches only)")
     ap.add_argument("--pow2", action="store_true", help="power-of-2 scales (quantizers round scales up to 2^k; "
@@ -531,6 +532,44 @@ def main():
             times.append(e0.elapsed_time(e1) / per_group)
         return float(np.median(times))
 
+    # Whole and partial rounds of output tiles. The step's Fprop is 1152 tiles of 256x256 on 256 compute
+    # units (4.5 rounds) and its Dgrad 448 (1.75 rounds); the same kernels over N = 16384 output columns
+    # (Fprop, 4 rounds) and K = 4096 (Dgrad, 1 round) show what the last, partly filled round costs.
+    tile_rounds = None
+    if not args.no_small:
+        tile_rounds = {}
+        Nw, Kw = 16384, 4096
+        ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+        w_k = w[:, :Kw].contiguous()
+        wkq = torch.empty((N, Kw), dtype=u8, device=dev)
+        wks = torch.empty((N // 128, Kw // 128), dtype=f32, device=dev)
+        y_w = torch.empty((M, Nw), dtype=torch.bfloat16, device=dev)
+        dx_w = torch.empty((M, Kw), dtype=f32, device=dev)
+        for mode, pw in (("fp32", False), ("pow2", True)):
+            fg.fg_quantize_fprop_operands(x, w, pow2=pw, q_cols=B["xq"], scales_cols=B["sx"], q_rows=B["xtq"],
+                                          scales_rows=B["sxt"], qw=B["wq"], sw=B["sw"])
+            fg.fg_quantize_act_1x128(dy, q=B["dyq"], scales=B["sdy"], pow2=pw)
+            fg.fg_quantize_w_128x128(w_k, q=wkq, scales=wks, pow2=pw)
+            wq_w, sw_w = B["wq"][:Nw], B["sw"][:Nw // 128]
+            res = {}
+            for name, fn, flop, tiles in [
+                ("fprop_N18432", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=pw),
+                 2.0 * M * N * K, (M // 256) * (N // 256)),
+                ("fprop_N16384", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], wq_w, sw_w, y=y_w, pow2=pw),
+                 2.0 * M * Nw * K, (M // 256) * (Nw // 256)),
+                ("dgrad_K7168", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], B["wq"], B["sw"], dx=B["dx"], pow2=pw),
+                 2.0 * M * N * K, (M // 256) * (K // 256)),
+                ("dgrad_K4096", lambda: fg.fg_fp8_gemm_dgrad(B["dyq"], B["sdy"], wkq, wks, dx=dx_w, pow2=pw),
+                 2.0 * M * N * Kw, (M // 256) * (Kw // 256)),
+            ]:
+                ms = back_to_back_ms(fn)
+                ach = flop / (ms * 1e-3) / 1e12
+                res[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4),
+                             "tile_rounds": round(tiles / ncu, 3)}
+            tile_rounds[mode] = res
+        del w_k, wkq, wks, y_w, dx_w
+        print("[bench] tile-round timings done", file=sys.stderr, flush=True)
+
     moe = None
     if not args.no_moe:
         del x, w, dy, bufs, B
@@ -660,6 +699,7 @@ def main():
         "vendor_fp8_gemm_reference": vendor,
         "moe_grouped": moe,
         "fprop_output_quantized": fused_epi,
+        "tile_rounds": tile_rounds,
         "per_tensor_contrast": per_tensor,
         "requantize_tokens": requant,
         "e5m6_storage": e5m6,
