@@ -898,6 +898,376 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void fg_gemm_kernel(GemmParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// Fprop on 256 x 288 x 128 workgroup tiles: 8 waves (4 x 2) of 64 x 144.
+//
+// The 256 x 256 shape runs one workgroup per CU, so a GEMM takes whole rounds of 256 tiles. The
+// DeepSeek-V3-like dense-MLP Fprop (N = 18432) is 4.5 such rounds, and its half-filled last round costs
+// nearly as much as a full one; 288 = 18432 / 64 covers the same output in exactly 4 rounds of tiles with
+// 12.5% more work each. A 144-column wave tile has 9 B fragments per K step, more than the registers left
+// beside its 144 accumulators can hold, so the operand roles of fg_gemm_kernel are swapped: a wave keeps
+// its four 16-row A fragments in registers for the whole K step and streams the nine 16-column B
+// fragments, each read one strip ahead of its MFMAs. Every output element still takes one scaled MFMA per
+// 128-K block and the same promotion (fma(P_b, RN(sA * sB), acc) with FP32 scales, the E8M0 operands
+// with power-of-2 scales) in the same block order, so the results equal the other shapes' bit for bit.
+// A 144-column wave tile can straddle two 128 x 128 weight blocks: each 16-column strip takes the scale of
+// the block it lies in.
+struct WideCfg {
+    static constexpr int WAVES_M = 4, WAVES_N = 2, WAVE_M = 64, WAVE_N = 144;
+    static constexpr int NW = WAVES_M * WAVES_N, NTHREADS = NW * 64;
+    static constexpr int BM = WAVES_M * WAVE_M, BN = WAVES_N * WAVE_N;       // 256 x 288
+    static constexpr int MSUB = WAVE_M / 16, NSUB = WAVE_N / 16;             // 4 x 9 MFMA tiles per wave
+    static constexpr int STAGE_A = BM * BK, STAGE_B = BN * BK, SCALES_A = BM * 4;
+    static constexpr int STAGE = STAGE_A + STAGE_B + SCALES_A;
+    static constexpr int LA = STAGE_A / 1024, LB = STAGE_B / 1024;
+    static constexpr int UA = (LA + NW - 1) / NW, UB = (LB + NW - 1) / NW;
+    static constexpr int SLICES_A = BM / 64;
+    static constexpr int LOADS_PER_WAVE = UA + UB + 1;
+    // epilogue: a wave re-lays 64 rows of BF16 (or 32 rows of FP32) of its tile in a private LDS region
+    static constexpr int OUT_REGION = 64 * WAVE_N * 2;
+    static constexpr int LDS_BYTES = 2 * STAGE > NW * OUT_REGION ? 2 * STAGE : NW * OUT_REGION;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(STAGE % 1024 == 0, "stages start on 1 KB boundaries");
+    static_assert(SLICES_A <= NW, "one scale slice per wave");
+};
+
+template <bool POW2, bool STREAM>
+__global__ __launch_bounds__(WideCfg::NTHREADS, 1) void fg_gemm_wide_kernel(GemmParams p) {
+    using C = WideCfg;
+    constexpr int BM = C::BM, BN = C::BN, NW = C::NW, MSUB = C::MSUB, NSUB = C::NSUB;
+    constexpr int WAVE_M = C::WAVE_M, WAVE_N = C::WAVE_N;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int nkb = (int)(K / BK);
+
+    // Tile order of fg_gemm_kernel's dense GEMMs: XCD-contiguous ranges of tile ids, walked in groups of 8
+    // M tiles, so the tiles an XCD runs at once share A and B panels in its L2.
+    const int n_tiles = (int)((N + BN - 1) / BN);
+    const int m_tiles = (int)((M + BM - 1) / BM);
+    const int id = xcd_remap((int)blockIdx.x, m_tiles * n_tiles);
+    constexpr int GM = 8;
+    const int group = id / (GM * n_tiles);
+    const int first_m = group * GM;
+    const int gsz = min(m_tiles - first_m, GM);
+    const int within = id - group * GM * n_tiles;
+    const int64_t m0 = (int64_t)(first_m + within % gsz) * BM;
+    const int64_t n0 = (int64_t)(within / gsz) * BN;
+
+    // LDS stage st: [A: BM rows x 128 B][B: BN rows x 128 B][A scales: BM floats]
+    auto stA = [&](int st) { return smem + st * C::STAGE; };
+    auto stB = [&](int st) { return smem + st * C::STAGE + C::STAGE_A; };
+    auto stSA = [&](int st) { return reinterpret_cast<float*>(smem + st * C::STAGE + C::STAGE_A + C::STAGE_B); };
+
+    // Global -> LDS load plan, as in fg_gemm_kernel: 1 KB (8 rows of 128 B) per direct-to-LDS instruction,
+    // instruction t of a wave = wave + NW u (a wave short of instructions re-issues its previous one), lane l
+    // at row 8t + l/8 fetching logical 16 B chunk (l % 8) ^ swz128(row); rows past the end re-read the last.
+    const uint8_t* a_tile = p.a + m0 * K;
+    const uint8_t* b_tile = p.b + n0 * K;
+    uint32_t a_off[C::UA], b_off[C::UB];
+    int a_t[C::UA], b_t[C::UB];
+#pragma unroll
+    for (int u = 0; u < C::UA; u++) {
+        int t = wave + NW * u;
+        t = t < C::LA ? t : t - NW;
+        a_t[u] = t;
+        const int row = t * 8 + (lane >> 3);
+        int64_t gr = m0 + row;
+        gr = gr < M ? gr : M - 1;
+        a_off[u] = (uint32_t)((gr - m0) * K + (((lane & 7) ^ swz128(row)) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < C::UB; u++) {
+        int t = wave + NW * u;
+        t = t < C::LB ? t : t - NW;
+        b_t[u] = t;
+        const int row = t * 8 + (lane >> 3);
+        int64_t gr = n0 + row;
+        gr = gr < N ? gr : N - 1;
+        b_off[u] = (uint32_t)((gr - n0) * K + (((lane & 7) ^ swz128(row)) << 4));
+    }
+    // A-row scales of one K step: wave w loads 64-float slice w % SLICES_A of the tile's BM rows
+    const int sc_slice = wave % C::SLICES_A;
+    int64_t sc_row = m0 + sc_slice * 64 + lane;
+    sc_row = sc_row < p.sa_ld ? sc_row : p.sa_ld - 1;
+    const uint32_t sc_off = (uint32_t)(sc_row * 4);
+    const int sc_dst = sc_slice * 256;
+    auto issue_load = [&](int kb, int st, int q) {
+        if (q < C::UA) {
+            const auto rs = fg_buffer_rsrc(a_tile + (int64_t)kb * BK);
+            fg_buffer_load_lds16(rs, stA(st) + a_t[q] * 1024, a_off[q]);
+        } else if (q < C::UA + C::UB) {
+            const int u = q - C::UA;
+            const auto rs = fg_buffer_rsrc(b_tile + (int64_t)kb * BK);
+            fg_buffer_load_lds16(rs, stB(st) + b_t[u] * 1024, b_off[u]);
+        } else {
+            const auto rs = fg_buffer_rsrc(p.sa + (int64_t)kb * p.sa_ld);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, FG_LDS(reinterpret_cast<uint8_t*>(stSA(st)) + sc_dst), 4, sc_off,
+                                                     0, 0, 0);
+        }
+    };
+    // The next step's loads go out in F pieces ahead of the first F strips of MFMAs (all before the last
+    // strip's hand-over barrier). F = 5 measured best with either scale mode on the dense-MLP Fprop (2-4%
+    // faster than 3 or 4 pieces; 8 pieces were 5% slower with FP32 scales).
+    constexpr int F = 5;
+    static_assert(F <= NSUB - 1, "the next stage's loads are all issued before the hand-over barrier");
+    auto issue_piece = [&](int kb, int st, int piece) {
+#pragma unroll
+        for (int q = piece * C::LOADS_PER_WAVE / F; q < (piece + 1) * C::LOADS_PER_WAVE / F; q++) issue_load(kb, st, q);
+    };
+
+    // Weight block scales: the wave's 144 columns [wave_n0, wave_n0 + 144) lie in blocks blk0 and blk1 =
+    // blk0 + 1 (wave_n0 is a multiple of 16, so at most two blocks); strip j lies in blk0 iff 16 j < split.
+    const int lrow = lane & 15;
+    const int lcol4 = (lane >> 4) * 4;
+    const int64_t wave_n0 = n0 + wn * WAVE_N;
+    const int64_t nblocks = (N + 127) / 128;
+    int64_t blk0 = wave_n0 / 128;
+    blk0 = blk0 < nblocks ? blk0 : nblocks - 1;
+    const int64_t blk1 = blk0 + 1 < nblocks ? blk0 + 1 : nblocks - 1;
+    const int split = 128 - (int)(wave_n0 & 127);
+    const float* sb_row0 = p.sb + blk0 * nkb;
+    const float* sb_row1 = p.sb + blk1 * nkb;
+
+    v4f acc[MSUB][NSUB];
+#pragma unroll
+    for (int i = 0; i < MSUB; i++)
+#pragma unroll
+        for (int j = 0; j < NSUB; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int g16 = lane >> 4;
+    const int frag_lo = lrow * BK + (((2 * g16) ^ swz128(lrow)) << 4);
+    const int frag_hi = lrow * BK + (((2 * g16 + 1) ^ swz128(lrow)) << 4);
+
+    // ---------------- main loop ----------------
+    // Step kb computes from stage kb & 1 while the loads of step kb + 1 fill the other stage. The barrier
+    // that hands the next stage over sits before the last strip of MFMAs: that strip's B fragment is already
+    // in registers, and the next step's A fragments are read after the MFMAs that last use each register.
+    v8i af[MSUB];                     // A fragments of the step, one per 16-row strip
+    float sa[MSUB];                   // their row scales (row lrow of each strip)
+    v8i bnext;                        // the next strip's B fragment
+    float sb0_next = 1.f, sb1_next = 1.f;
+    uint32_t bad_scale = 0;           // power-of-2 mode: sign or mantissa bits seen in any scale
+    auto read_a = [&](int st, int i) {
+        af[i] = frag_at(stA(st) + (wm * WAVE_M + i * 16) * BK, frag_lo, frag_hi);
+        sa[i] = stSA(st)[wm * WAVE_M + i * 16 + lrow];
+    };
+    auto read_b = [&](int st, int j) -> v8i { return frag_at(stB(st) + (wn * WAVE_N + j * 16) * BK, frag_lo, frag_hi); };
+    if (nkb > 0) {
+#pragma unroll
+        for (int q = 0; q < C::LOADS_PER_WAVE; q++) issue_load(0, 0, q);
+        sb0_next = sb_row0[0];
+        sb1_next = sb_row1[0];
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MSUB; i++) read_a(0, i);
+        bnext = read_b(0, 0);
+    }
+    // FP32 scales: the wave raises its priority while a strip of MFMAs issues, as in fg_gemm_kernel.
+    // Power-of-2 scales keep the default priority (measured on the dense-MLP Fprop: 2% faster there, 2%
+    // slower with FP32 scales).
+    constexpr int MFMA_PRIO = POW2 ? 0 : 3;
+    auto step = [&](int kb, auto more_tag) {
+        constexpr bool more = decltype(more_tag)::value;
+        const int st = kb & 1;
+        const float sb0 = sb0_next, sb1 = sb1_next;
+        if (more) {
+            sb0_next = sb_row0[kb + 1];
+            sb1_next = sb_row1[kb + 1];
+        }
+        int ea[MSUB];
+        int eb0 = 0, eb1 = 0;
+        if constexpr (POW2) {
+#pragma unroll
+            for (int i = 0; i < MSUB; i++) ea[i] = e8m0_of(sa[i], bad_scale);
+            eb0 = e8m0_of(sb0, bad_scale);
+            eb1 = e8m0_of(sb1, bad_scale);
+        }
+        // FP32 scales: tile-lagged promotion, the FMAs issued after MFMA t folding tile t - 4 (a VALU read of
+        // an MFMA result waits for the whole MFMA). Measured on the dense-MLP Fprop against lags of 2 and 3
+        // and against interleave hints (one MFMA, five VALU operations): 3-5% faster than a lag of 2, and the
+        // only one faster than the 256 x 256 shape; the pending tiles fill the register file to its 256.
+        constexpr int LAG = 4;
+        v4f pend[LAG];
+        float pend_s[LAG];
+        int pend_i[LAG], pend_j[LAG];
+#pragma unroll
+        for (int l = 0; l < LAG; l++) pend_i[l] = -1;
+#pragma unroll
+        for (int j = 0; j < NSUB; j++) {
+            if (more && j < F) issue_piece(kb + 1, st ^ 1, j);
+            const v8i bcur = bnext;
+            if (j + 1 < NSUB) bnext = read_b(st, j + 1);
+            constexpr int LAST = NSUB - 1;
+            if (more && j == LAST) {
+                // every read of this stage is done and this wave's next-stage loads have landed; then every
+                // wave's (the fences keep earlier MFMAs from moving past the barrier)
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const bool in0 = 16 * j < split;
+            if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(MFMA_PRIO);
+#pragma unroll
+            for (int i = 0; i < MSUB; i++) {
+                if constexpr (POW2) {
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, af[i], acc[i][j], 0, 0, 0,
+                                                                                in0 ? eb0 : eb1, 0, ea[i]);
+                } else {
+                    const v4f cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, af[i], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                                     0, 0, 0, 127, 0, 127);
+                    constexpr int O = LAG - 1;
+                    if (pend_i[O] >= 0) {
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            acc[pend_i[O]][pend_j[O]][r] = __builtin_fmaf(pend[O][r], pend_s[O], acc[pend_i[O]][pend_j[O]][r]);
+                    }
+#pragma unroll
+                    for (int l = O; l > 0; l--) {
+                        pend[l] = pend[l - 1];
+                        pend_s[l] = pend_s[l - 1];
+                        pend_i[l] = pend_i[l - 1];
+                        pend_j[l] = pend_j[l - 1];
+                    }
+                    pend[0] = cur;
+                    pend_s[0] = sa[i] * (in0 ? sb0 : sb1);
+                    pend_i[0] = i;
+                    pend_j[0] = j;
+                }
+                if (more && j == LAST) read_a(st ^ 1, i);
+            }
+            if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
+            if (more && j == LAST) bnext = read_b(st ^ 1, 0);
+        }
+        if constexpr (!POW2) {
+#pragma unroll
+            for (int l = LAG - 1; l >= 0; l--)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    acc[pend_i[l]][pend_j[l]][r] = __builtin_fmaf(pend[l][r], pend_s[l], acc[pend_i[l]][pend_j[l]][r]);
+        }
+    };
+    for (int kb = 0; kb + 1 < nkb; kb++) step(kb, fg_bool<true>{});
+    if (nkb > 0) step(nkb - 1, fg_bool<false>{});
+
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (POW2) {
+        // a scale that is not a positive power of two: the wave's whole output tile becomes NaN
+        if (__builtin_amdgcn_ballot_w64(bad_scale != 0) != 0) {
+#pragma unroll
+            for (int i = 0; i < MSUB; i++)
+#pragma unroll
+                for (int j = 0; j < NSUB; j++) acc[i][j] = v4f{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                               __builtin_nanf("")};
+        }
+    }
+
+    // ---------------- epilogue ----------------
+    // A wave whose 144 columns lie inside the output re-lays its tile in a private LDS region (64 rows of
+    // 288 B for BF16; FP32 in two halves of 32 rows of 576 B) and stores it as contiguous 16-byte chunks:
+    // the region is dense, so chunk f of it is row f / (chunks per row), and one store instruction writes
+    // whole 288 B or 576 B row segments instead of 16 rows x 32 B (BF16) or 16 rows x 64 B (FP32) from the
+    // MFMA layout. The values are only moved. The condition of the barrier is uniform over the workgroup.
+    const bool bf16 = p.out_bf16 != 0;
+    if (bf16 ? (N & 7) == 0 : (N & 3) == 0) {
+        __syncthreads();                    // the stages are free: every wave's last fragment reads are done
+        if (wave_n0 + WAVE_N <= N) {
+            uint8_t* reg = smem + wave * C::OUT_REGION;
+            const int64_t mw = m0 + wm * WAVE_M;
+            if (bf16) {
+                constexpr int RB = WAVE_N * 2, CPR = RB / 16;          // 288 B, 18 chunks per row
+                uint16_t* o = reinterpret_cast<uint16_t*>(p.out);
+#pragma unroll
+                for (int i = 0; i < MSUB; i++)
+#pragma unroll
+                    for (int j = 0; j < NSUB; j++) {
+                        uint2 v;
+                        v.x = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
+                        v.y = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
+                        *reinterpret_cast<uint2*>(reg + (i * 16 + lrow) * RB + (j * 16 + lcol4) * 2) = v;
+                    }
+#pragma unroll
+                for (int k = 0; k < 64 * CPR / 64; k++) {
+                    const int f = 64 * k + lane;
+                    const int r = f / CPR, c = f % CPR;
+                    const uint4 v = *reinterpret_cast<const uint4*>(reg + 16 * f);
+                    const int64_t m = mw + r;
+                    if (m < M) {
+                        if constexpr (STREAM)   // an output too large to stay cached (see launch())
+                            __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(o + m * N + wave_n0 + c * 8));
+                        else
+                            *reinterpret_cast<uint4*>(o + m * N + wave_n0 + c * 8) = v;
+                    }
+                }
+            } else {
+                constexpr int RB = WAVE_N * 4, CPR = RB / 16;          // 576 B, 36 chunks per row
+                float* o = reinterpret_cast<float*>(p.out);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+#pragma unroll
+                    for (int i = 0; i < 2; i++)
+#pragma unroll
+                        for (int j = 0; j < NSUB; j++)
+                            *reinterpret_cast<v4f*>(reg + (i * 16 + lrow) * RB + (j * 16 + lcol4) * 4) = acc[2 * h + i][j];
+#pragma unroll
+                    for (int k = 0; k < 32 * CPR / 64; k++) {
+                        const int f = 64 * k + lane;
+                        const int r = f / CPR, c = f % CPR;
+                        const v4f v = *reinterpret_cast<const v4f*>(reg + 16 * f);
+                        const int64_t m = mw + 32 * h + r;
+                        if (m < M) {
+                            if constexpr (STREAM)
+                                __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(o + m * N + wave_n0 + c * 4));
+                            else
+                                *reinterpret_cast<float4*>(o + m * N + wave_n0 + c * 4) = make_float4(v[0], v[1], v[2], v[3]);
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
+    // Straight from the MFMA layout (a wave tile that runs past N, or unaligned output rows): lane l holds
+    // row lrow and columns lcol4 .. lcol4 + 3 of every 16 x 16 tile.
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < MSUB; i++) {
+        const int64_t m = m0 + wm * WAVE_M + i * 16 + lrow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NSUB; j++) {
+            const int64_t n = wave_n0 + j * 16 + lcol4;
+            if (bf16) {
+                uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * N + n;
+                if (vec_ok && n + 3 < N) {
+                    uint2 v;
+                    v.x = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
+                    v.y = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
+                    *reinterpret_cast<uint2*>(o) = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        if (n + r < N) o[r] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
+                }
+            } else {
+                float* o = reinterpret_cast<float*>(p.out) + m * N + n;
+                if (vec_ok && n + 3 < N) {
+                    *reinterpret_cast<float4*>(o) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        if (n + r < N) o[r] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
 template <class C, bool B_TRANS, int SBK, int GROUP, bool POW2, int EPI = EPI_STORE, bool STREAM = false>
 hipError_t launch_one(const GemmParams& p, unsigned grid, hipStream_t stream) {
     auto kern = fg_gemm_kernel<C, B_TRANS, SBK, GROUP, POW2, EPI, STREAM>;
@@ -963,6 +1333,34 @@ hipError_t launch(const GemmParams& p, int pow2, hipStream_t stream) {
                 : launch_one<Cfg12, B_TRANS, SBK, GROUP, false>(p, grid, stream);
 }
 
+// Fprop on 256 x 288 tiles (fg_gemm_wide_kernel) when they need fewer tile-work units than the 8-wave
+// 256 x 256 shape: rounds of tiles over the CUs times the tile's area, as in use_cfg8. At the dense-MLP
+// Fprop (M = 4096, N = 18432) that is 4 rounds of 256 x 288 against 4.5 (counted as 5) of 256 x 256.
+// FG_GEMM_TILE=256x288 forces it; FG_GEMM_TILE=256x192 or 256x256 rules it out. Its B operand offsets
+// reach 287 K, so contractions with 288 K >= 2^32 keep the other shapes.
+bool use_wide(const GemmParams& p) {
+    if ((int64_t)WideCfg::BN * p.K >= (1ll << 32)) return false;
+    const char* force = getenv("FG_GEMM_TILE");
+    if (force && strcmp(force, "256x288") == 0) return true;
+    if (force && (strcmp(force, "256x256") == 0 || strcmp(force, "256x192") == 0)) return false;
+    if (!use_cfg8(p, GRP_NONE)) return false;
+    const int64_t cus = fg_device_cus();
+    const int64_t m_tiles = (p.M + 255) / 256;
+    const int64_t rw = (m_tiles * ((p.N + WideCfg::BN - 1) / WideCfg::BN) + cus - 1) / cus;
+    const int64_t r8 = (m_tiles * ((p.N + Cfg8::BN - 1) / Cfg8::BN) + cus - 1) / cus;
+    return rw * WideCfg::BN < r8 * Cfg8::BN;
+}
+
+template <bool POW2, bool STREAM>
+hipError_t launch_wide(const GemmParams& p, unsigned grid, hipStream_t stream) {
+    auto kern = fg_gemm_wide_kernel<POW2, STREAM>;
+    static std::atomic<uint64_t> lds_limit_set{0};
+    const hipError_t e = fg_set_lds_limit_once((const void*)kern, WideCfg::LDS_BYTES, lds_limit_set);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WideCfg::NTHREADS), WideCfg::LDS_BYTES, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw, int64_t M,
@@ -970,6 +1368,13 @@ hipError_t fg_launch_gemm_fprop(const uint8_t* xq, const float* sx, const uint8_
     GemmParams p{};
     p.a = xq; p.sa = sx; p.sa_ld = M; p.b = wq; p.sb = sw;
     p.M = M; p.N = N; p.K = K; p.out = y; p.out_bf16 = out_bf16;
+    if (use_wide(p)) {
+        const unsigned grid = (unsigned)(((M + WideCfg::BM - 1) / WideCfg::BM) * ((N + WideCfg::BN - 1) / WideCfg::BN));
+        const bool stream_out = M * N * (out_bf16 ? 2 : 4) >= kStreamOutBytes;
+        if (stream_out)
+            return pow2 ? launch_wide<true, true>(p, grid, stream) : launch_wide<false, true>(p, grid, stream);
+        return pow2 ? launch_wide<true, false>(p, grid, stream) : launch_wide<false, false>(p, grid, stream);
+    }
     return launch<false, SB_BLOCK, GRP_NONE>(p, pow2, stream);
 }
 

@@ -60,9 +60,10 @@
  * return FG_ERR_UNSUPPORTED_SHAPE.
  *
  * Every GEMM picks one of two workgroup tiles per launch (256x192 or 256x256 outputs) from the problem size
- * and the device's compute-unit count; the results are bit-identical either way (every output element
- * goes through the same instructions in the same order). The environment
- * variable FG_GEMM_TILE=256x192 or FG_GEMM_TILE=256x256 forces one (read at every launch).
+ * and the device's compute-unit count, and fg_fp8_gemm_fprop a third (256x288) where it covers the output
+ * in fewer rounds of tiles over the compute units; the results are bit-identical whichever is used (every
+ * output element goes through the same instructions in the same order). The environment variable
+ * FG_GEMM_TILE=256x192, 256x256 or 256x288 (Fprop only) forces one (read at every launch).
  *
  * Layouts are row-major. "ld" arguments are row strides in elements.
  * Activation scales are MN-major: scale[group][row] (rows contiguous), so one 128-deep K step of a GEMM

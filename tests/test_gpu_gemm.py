@@ -42,9 +42,11 @@ def _cmp(y_gpu, prom, bf16, tol_scale=1.0):
 
 
 # The library picks one of two workgroup shapes per launch (256x192 with 12 waves, 256x256 with 8 waves)
-# from the problem size; FG_GEMM_TILE forces one. Small shapes run under both, and under the automatic
-# choice; the full-size cases run under the automatic choice, the configuration the benchmark times.
+# from the problem size, and for Fprop a third (256x288, 8 waves of 64x144); FG_GEMM_TILE forces one.
+# Small shapes run under each, and under the automatic choice; the full-size cases run under the automatic
+# choice, the configuration the benchmark times (256x288 for the dense-MLP Fprop).
 TILES = ["auto", "256x192", "256x256"]
+FPROP_TILES = TILES + ["256x288"]
 
 
 @pytest.fixture
@@ -92,20 +94,22 @@ def test_fprop_tiny_config_fp32():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (37, 130, 256), (256, 256, 128), (300, 520, 384),
-                                   (513, 260, 640), (64, 1000, 1024), (1000, 64, 128)])
+                                   (513, 260, 640), (64, 1000, 1024), (1000, 64, 128), (300, 576, 384),
+                                   (129, 1152, 512)])
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("tile", TILES, indirect=True)
+@pytest.mark.parametrize("tile", FPROP_TILES, indirect=True)
 def test_fprop_shapes(M, N, K, bf16, tile):
     device()
     rng = np.random.default_rng(M * 31 + N * 7 + K)
     _fprop_case(_rand_act(rng, M, K), wl.normal_bf16(rng, (N, K), 0.02), bf16)
 
 
-@pytest.mark.parametrize("tile", TILES, indirect=True)
+@pytest.mark.parametrize("tile", FPROP_TILES, indirect=True)
 def test_fprop_pow2_scales(tile):
     device()
     rng = np.random.default_rng(9)
     _fprop_case(_rand_act(rng, 200, 512), wl.normal_bf16(rng, (384, 512), 0.02), bf16=False, pow2=True)
+    _fprop_case(_rand_act(rng, 300, 384), wl.normal_bf16(rng, (576, 384), 0.02), bf16=True, pow2=True)
 
 
 def test_fprop_closed_form_all_ones():
@@ -482,7 +486,7 @@ def test_grouped_offsets_clamped_on_device():
 # Power-of-2 mode handed scales that are not powers of two: NaN outputs, not silently wrong sums
 # ------------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("tile", TILES, indirect=True)
+@pytest.mark.parametrize("tile", FPROP_TILES, indirect=True)
 def test_pow2_mode_poisons_tiles_with_other_scales(tile):
     """Power-of-2 codes and scales, with one activation row's scale given mantissa bits: every output of
     the wave tiles that read that scale is NaN, every other output equals the clean run bit for bit."""
@@ -533,6 +537,28 @@ def test_pow2_mode_with_fp32_scales_is_nan_everywhere():
         assert torch.isnan(t.float()).all(), name
     assert torch.isnan(sy).all()
     assert bool(((yq & 0x7F) == 0x7F).all()), "quantizing Fprop: NaN codes"
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 640), (300, 576, 384), (513, 1152, 256)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_fprop_wide_tile_bit_identical(M, N, K, pow2, monkeypatch):
+    """Fprop on 256x288 tiles (each wave keeps its A fragments and streams B) gives the 256x256 shape's
+    outputs bit for bit, for both output types: ragged rows, and columns that end inside a wave tile, on a
+    wave-tile boundary, or on a workgroup-tile boundary (staged and direct stores)."""
+    device()
+    rng = np.random.default_rng(M + N + K)
+    xq, sx = fg.fg_quantize_act_1x128(to_dev(_rand_act(rng, M, K)), pow2=pow2)
+    wq, sw = fg.fg_quantize_w_128x128(to_dev(wl.normal_bf16(rng, (N, K), 0.02)), pow2=pow2)
+    outs = {}
+    for val in ("256x256", "256x288"):
+        monkeypatch.setenv("FG_GEMM_TILE", val)
+        outs[val] = [fg.fg_fp8_gemm_fprop(xq, sx, wq, sw, y=nan_like_out((M, N), dt), pow2=pow2)
+                     for dt in (torch.float32, torch.bfloat16)]
+        torch.cuda.synchronize()
+    for a, b in zip(outs["256x256"], outs["256x288"]):
+        assert_all_written(b, "fprop 256x288")
+        iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a.view(iv), b.view(iv)), a.dtype
 
 
 @pytest.mark.parametrize("pow2", [False, True])
