@@ -532,9 +532,11 @@ def main():
             times.append(e0.elapsed_time(e1) / per_group)
         return float(np.median(times))
 
-    # Whole and partial rounds of output tiles. The step's Fprop is 1152 tiles of 256x256 on 256 compute
-    # units (4.5 rounds) and its Dgrad 448 (1.75 rounds); the same kernels over N = 16384 output columns
-    # (Fprop, 4 rounds) and K = 4096 (Dgrad, 1 round) show what the last, partly filled round costs.
+    # Whole and partial rounds of output tiles. On 256x256 tiles (forced here) the step's Fprop is 1152
+    # tiles on 256 compute units (4.5 rounds) and its Dgrad 448 (1.75 rounds); the same kernels over
+    # N = 16384 output columns (Fprop, 4 rounds) and K = 4096 (Dgrad, 1 round) show what the last, partly
+    # filled round costs. The library's own choice for the step's Fprop, 1024 tiles of 256x288 (4 rounds),
+    # is timed beside them.
     tile_rounds = None
     if not args.no_small:
         tile_rounds = {}
@@ -552,6 +554,8 @@ def main():
             fg.fg_quantize_w_128x128(w_k, q=wkq, scales=wks, pow2=pw)
             wq_w, sw_w = B["wq"][:Nw], B["sw"][:Nw // 128]
             res = {}
+            tile_env = os.environ.pop("FG_GEMM_TILE", None)
+            os.environ["FG_GEMM_TILE"] = "256x256"
             for name, fn, flop, tiles in [
                 ("fprop_N18432", lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=pw),
                  2.0 * M * N * K, (M // 256) * (N // 256)),
@@ -565,7 +569,16 @@ def main():
                 ms = back_to_back_ms(fn)
                 ach = flop / (ms * 1e-3) / 1e12
                 res[name] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1), "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4),
-                             "tile_rounds": round(tiles / ncu, 3)}
+                             "tile_rounds": round(tiles / ncu, 3), "tile": "256x256"}
+            os.environ["FG_GEMM_TILE"] = "256x288"
+            ms = back_to_back_ms(lambda: fg.fg_fp8_gemm_fprop(B["xq"], B["sx"], B["wq"], B["sw"], y=B["y"], pow2=pw))
+            del os.environ["FG_GEMM_TILE"]
+            if tile_env is not None:
+                os.environ["FG_GEMM_TILE"] = tile_env
+            ach = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            res["fprop_N18432_256x288"] = {"ms": round(ms, 4), "TFLOP/s": round(ach, 1),
+                                           "frac_fp8_peak": round(ach / PEAK_FP8_TFLOPS, 4),
+                                           "tile_rounds": round((M // 256) * (N // 288) / ncu, 3), "tile": "256x288"}
             tile_rounds[mode] = res
         del w_k, wkq, wks, y_w, dx_w
         print("[bench] tile-round timings done", file=sys.stderr, flush=True)

@@ -183,7 +183,8 @@ def _dgrad_case(dy, w, bf16, pts=None, pow2=False):
     return _cmp(yo, prom, bf16), yo, exact
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (37, 256, 128), (300, 384, 640), (256, 128, 256), (100, 512, 384)])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (37, 256, 128), (300, 384, 640), (256, 128, 256), (100, 512, 384),
+                                   (300, 256, 896), (129, 384, 1152)])
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("tile", TILES, indirect=True)
