@@ -154,6 +154,20 @@ def test_fprop_dsv3_full_size_sampled(dsv3, pow2):
     assert normwise(bf16_bits_to_f64(y), exact) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,N,bf16", [(8960, 16704, True), (4096, 18432, False), (16384, 8192, True)])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_fprop_output_past_cache_size(M, N, bf16, pow2):
+    """Outputs of 256 MiB or more are stored past the caches (a separate instantiation of each kernel):
+    299 MB of BF16 and 302 MB of FP32 on 256x288 tiles, 268 MB of BF16 on 256x256 tiles, each tile the
+    library's own choice on 256 compute units. K = 256 keeps the oracle's sampled check cheap; every 64x64 output block
+    is sampled and the NaN-filled output must come back entirely written."""
+    device()
+    rng = np.random.default_rng(M + N + (7 if bf16 else 3))
+    K = 256
+    pts = stratified_points(M, N, 2000, seed=17)
+    _fprop_case(_rand_act(rng, M, K), wl.normal_bf16(rng, (N, K), 0.02), bf16=bf16, pow2=pow2, pts=pts)
+
+
 def test_fprop_deterministic(dsv3):
     x, w, _ = dsv3
     xq, sx = fg.fg_quantize_act_1x128(to_dev(x))
