@@ -112,7 +112,8 @@ def test_fprop_pow2_scales(tile):
     _fprop_case(_rand_act(rng, 300, 384), wl.normal_bf16(rng, (576, 384), 0.02), bf16=True, pow2=True)
 
 
-def test_fprop_closed_form_all_ones():
+@pytest.mark.parametrize("tile", FPROP_TILES, indirect=True)
+def test_fprop_closed_form_all_ones(tile):
     # every code 1.0 (bf16 ones quantize to code 0x7E with scale 1/448): Y = K exactly
     device()
     M, N, K = 100, 300, 1024
@@ -126,7 +127,8 @@ def test_fprop_closed_form_all_ones():
     assert np.allclose(y, K, rtol=1e-6)
 
 
-def test_fprop_zero_k_writes_zeros():
+@pytest.mark.parametrize("tile", FPROP_TILES, indirect=True)
+def test_fprop_zero_k_writes_zeros(tile):
     device()
     y = torch.full((5, 7), 3.0, device=device())
     xq = torch.empty((5, 0), dtype=torch.uint8, device=device())
