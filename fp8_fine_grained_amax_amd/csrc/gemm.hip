@@ -1010,8 +1010,8 @@ __global__ __launch_bounds__(WideCfg::NTHREADS, 1) void fg_gemm_wide_kernel(Gemm
         }
     };
     // The next step's loads go out in F pieces ahead of the first F strips of MFMAs (all before the last
-    // strip's hand-over barrier). F = 5 measured best with either scale mode on the dense-MLP Fprop (2-4%
-    // faster than 3 or 4 pieces; 8 pieces were 5% slower with FP32 scales).
+    // strip's hand-over barrier). F = 5 measured best with either scale mode on the dense-MLP Fprop (1-2%
+    // faster than 3 or 4 pieces, 3-9% faster than 6 to 8).
     constexpr int F = 5;
     static_assert(F <= NSUB - 1, "the next stage's loads are all issued before the hand-over barrier");
     auto issue_piece = [&](int kb, int st, int piece) {
