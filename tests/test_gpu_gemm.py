@@ -246,7 +246,8 @@ def _wgrad_case(dy, x, pts=None, init=None, pow2=False):
     return _cmp(yo, prom, False), yo, exact
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 8, 8), (128, 40, 264), (256, 296, 384), (384, 256, 128), (512, 136, 72)])
+@pytest.mark.parametrize("M,N,K", [(128, 8, 8), (128, 40, 264), (256, 296, 384), (384, 256, 128), (512, 136, 72),
+                                   (384, 520, 640)])
 @pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("tile", TILES, indirect=True)
 def test_wgrad_shapes(M, N, K, pow2, tile):
