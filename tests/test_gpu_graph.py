@@ -24,8 +24,12 @@ def _step(x, w, dy, pow2):
     return [xq, sx, xtq, sxt, wq, sw, y, dyq, sdy, dytq, sdyt, dx, dw]
 
 
+@pytest.mark.parametrize("tile", ["auto", "256x288"])
 @pytest.mark.parametrize("pow2", [False, True])
-def test_step_graph_replays_match_eager(pow2):
+def test_step_graph_replays_match_eager(pow2, tile, monkeypatch):
+    """"256x288" forces the Fprop onto its wide tile (the other GEMMs ignore that setting)."""
+    if tile != "auto":
+        monkeypatch.setenv("FG_GEMM_TILE", tile)
     device()
     rng = np.random.default_rng(71)
     M, N, K = 640, 896, 1152
